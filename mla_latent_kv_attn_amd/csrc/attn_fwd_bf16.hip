@@ -1,0 +1,230 @@
+// attn_fwd_bf16.hip - bf16 fused attention forward on the matrix cores.
+//
+// Computes O = softmax(scale Q K^T) V (optional causal mask) and the per-row
+// log-sum-exp, [FA2-v2 blog] sections 1.1-3.5, with bf16 inputs, fp32
+// accumulation and a bf16 output.  The blog stops at CUDA cores and names
+// tensor-core MMA as its next step (sections 1.3 and 5); this is that step
+// written for CDNA4 matrix cores.
+//
+// Tiling (D = 128): a workgroup owns Br = 128 query rows of one (b, h);
+// wave w owns rows 32w..32w+31.  Key/value tiles of Bc = 64 rows are copied
+// global -> LDS (global_load_lds_dwordx4) into a double buffer.
+//
+// Products per wave and 64-key tile (v_mfma_f32_32x32x16_bf16):
+//   S^T = K Q^T  : A = K rows from LDS, B = Q held in VGPRs.  The result
+//                  puts one query per lane column, so a query's row max and
+//                  sum need one exchange (lanes l and l^32).
+//   O^T += V^T P^T: A = V^T read with ds_read_b64_tr_b16 straight from the
+//                  row-major V tile; B = P^T, which is the S^T accumulator
+//                  rounded to bf16 with no data movement (see the key
+//                  permutation below).
+// Softmax runs in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e).
+// The accumulator is rescaled only when some row max of the wave grew.
+// Masks follow section 3.4: tiles past the causal limit are never loaded;
+// the element mask is applied only on tiles that straddle the diagonal; keys
+// past N are clamped on load and masked.  A tile whose keys are all masked
+// for every row of a wave is skipped by that wave.
+#include "common.h"
+
+namespace mla {
+
+constexpr int B16_D = 128;
+constexpr int B16_BR = 128;
+constexpr int B16_BC = 64;
+constexpr int B16_WAVES = 4;
+constexpr int B16_THREADS = 64 * B16_WAVES;
+constexpr int B16_ROW_CHUNKS = B16_D * 2 / 16;                       // 16 chunks of 16 B per row
+constexpr int B16_STRIDE = (B16_ROW_CHUNKS + 1) * 16;                // 272 B per LDS row (== 16 mod 128)
+constexpr int B16_TILE_BYTES = B16_BC * B16_STRIDE;                  // 17408
+constexpr int B16_TILE_INSTR = B16_BC * (B16_ROW_CHUNKS + 1) / 64;   // 17 wave-wide 1 KiB copies per tile
+static_assert(B16_BC * (B16_ROW_CHUNKS + 1) % 64 == 0, "whole copies");
+static_assert(B16_TILE_INSTR % B16_WAVES == 1, "wave 0 issues the one extra copy");
+constexpr int B16_LOADS_HI = 2 * ((B16_TILE_INSTR + B16_WAVES - 1) / B16_WAVES);  // K + V copies, wave 0
+constexpr int B16_LOADS_LO = 2 * (B16_TILE_INSTR / B16_WAVES);                    // other waves
+
+// LDS rows have a stride of 16 (mod 128) bytes.  Inside each 32-key block
+// MFMA row rho = 16a + 8b + 4g + c is fed key 16a + 8b + g + 2c, so that
+// (i) the eight rows one 8-lane group reads for S^T = K Q^T fall on eight
+// distinct 16-byte bank groups, (ii) register e of lane group g of S^T
+// holds key 16(e/8) + 8((e/4)%2) + g + 2(e%4), i.e. the eight registers of
+// k-step e/8 are P^T with logical k index 8g + e%8, and (iii) the four rows
+// each transposed V read touches are two apart, on distinct 32-byte groups.
+__device__ __forceinline__ int b16_kappa32(int rho) { return (rho & ~7) + ((rho >> 2) & 1) + 2 * (rho & 3); }
+__device__ __forceinline__ int b16_key_of_reg(int e, int g) {
+    return 16 * (e >> 3) + 8 * ((e >> 2) & 1) + g + 2 * (e & 3);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, int num_q_tiles, float c_log2) {
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][B16_TILE_BYTES];  // [buf][K|V]
+
+    // Work mapping: the id's low part is batch*head, so every (b,h) stays on
+    // one XCD (ids are dealt round-robin over the XCDs); causal tiles are
+    // dealt heaviest first.
+    const int id = blockIdx.x;
+    const int bh = id % BH;
+    const int rank = id / BH;
+    const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+    const int q_start = qt * B16_BR;
+    const size_t base = (size_t)bh * N * B16_D;
+
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int n = lane & 31;  // query column of the MFMA results
+    const int g = lane >> 5;  // row group
+    const int wrow0 = q_start + 32 * w;
+
+    // Q as the B operand of S^T = K Q^T: lane holds row wrow0+n, dims 16kk+8g..+7.
+    bf16x8 qf[B16_D / 16];
+    {
+        const int r = min(wrow0 + n, N - 1);
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + base + (size_t)r * B16_D);
+#pragma unroll
+        for (int kk = 0; kk < B16_D / 16; ++kk) qf[kk] = qp[2 * kk + g];
+    }
+
+    const int kv_limit = CAUSAL ? min(q_start + B16_BR, N) : N;
+    const int Tc = (kv_limit + B16_BC - 1) / B16_BC;
+
+    // Copy i (0..16) of 64 chunks of the K and of the V tile is issued by wave
+    // i % 4.  Chunk L is row L / 17, chunk L % 17 (the pad chunk 16 repeats
+    // chunk 0).  Keys past N repeat key N-1 and are masked.
+    auto issue_tile = [&](int j, int buf) {
+        const int kv_start = j * B16_BC;
+        for (int i = w; i < B16_TILE_INSTR; i += B16_WAVES) {
+            const int L = i * 64 + lane;
+            const int r = L / (B16_ROW_CHUNKS + 1);
+            int c = L - r * (B16_ROW_CHUNKS + 1);
+            c = (c == B16_ROW_CHUNKS) ? 0 : c;
+            const size_t grow = base + (size_t)min(kv_start + r, N - 1) * B16_D + 8 * c;
+            gload_lds16(k + grow, &smem[buf][0][i * 1024]);
+            gload_lds16(v + grow, &smem[buf][1][i * 1024]);
+        }
+    };
+
+    f32x16 oacc[B16_D / 32];
+#pragma unroll
+    for (int db = 0; db < B16_D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    float m = -INFINITY;  // running max, already scaled into the log2 domain
+    float l = 0.f;        // this lane's share of the running sum
+
+    // Per-lane LDS byte offsets (all other offsets are immediates).
+    const int k_off = b16_kappa32(n) * B16_STRIDE + 16 * g;
+    const int G = lane >> 4, sl = lane & 15;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
+    const int jj = sl >> 2, qd = sl & 3;
+    const int v_off = ((G >> 1) + 2 * jj) * B16_STRIDE + 32 * (G & 1) + 8 * qd;
+
+    issue_tile(0, 0);
+    for (int j = 0; j < Tc; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < Tc) {
+            issue_tile(j + 1, buf ^ 1);
+            if (w == 0) wait_vmcnt<B16_LOADS_HI>();
+            else wait_vmcnt<B16_LOADS_LO>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+
+        const int kv_start = j * B16_BC;
+        const bool wave_dead = CAUSAL && (kv_start > wrow0 + 31);
+        if (!wave_dead) {
+            const char* Kt = smem[buf][0] + k_off;
+            const char* Vt = smem[buf][1] + v_off;
+            f32x16 s0, s1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+            for (int kk = 0; kk < B16_D / 16; ++kk) {
+                s0 = mfma32(lds_read16(Kt, 32 * kk), qf[kk], s0);
+                s1 = mfma32(lds_read16(Kt, 32 * B16_STRIDE + 32 * kk), qf[kk], s1);
+            }
+            const bool tail = kv_start + B16_BC > N;
+            const bool diag = CAUSAL && (kv_start + B16_BC - 1 > wrow0);
+            if (tail || diag) {
+                const int row = wrow0 + n;
+                const int lim = diag ? min(row + 1, N) : N;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kv_start + b16_key_of_reg(e, g);
+                    if (key >= lim) s0[e] = -INFINITY;
+                    if (key + 32 >= lim) s1[e] = -INFINITY;
+                }
+            }
+            float mt = fmaxf(s0[0], s1[0]);
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
+            mt = max2_halves(mt) * c_log2;
+            const float m_new = fmaxf(m, mt);
+            const float mb = (m_new == -INFINITY) ? 0.f : m_new;
+            if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+                const float alpha = fast_exp2(m - mb);
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < B16_D / 32; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            }
+            m = m_new;
+            bf16x8 pb[4];  // k-step ks (keys 16ks..16ks+15 of the tile)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p0 = fast_exp2(__builtin_fmaf(s0[e], c_log2, -mb));
+                const float p1 = fast_exp2(__builtin_fmaf(s1[e], c_log2, -mb));
+                l += p0 + p1;
+                pb[(e >> 3)][e & 7] = to_bf16(p0);
+                pb[2 + (e >> 3)][e & 7] = to_bf16(p1);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                for (int db = 0; db < B16_D / 32; ++db) {
+                    bf16x4 lo = lds_read_tr16(Vt, 16 * ks * B16_STRIDE + 64 * db);
+                    bf16x4 hi = lds_read_tr16(Vt, (16 * ks + 8) * B16_STRIDE + 64 * db);
+                    oacc[db] = mfma32(join(lo, hi), pb[ks], oacc[db]);
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    // Epilogue: O = Oacc / l; O^T register e of block db: dim 32db + 8(e/4) + 4g + e%4.
+    l = sum2_halves(l);
+    const int row = wrow0 + n;
+    if (row < N) {
+        const float inv_l = 1.f / l;
+        __bf16* op = o + base + (size_t)row * B16_D;
+#pragma unroll
+        for (int db = 0; db < B16_D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16x4 t;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][4 * i + r] * inv_l);
+                *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i + 4 * g) = t;
+            }
+        if (lse && g == 0) lse[(size_t)bh * N + row] = (m + __builtin_log2f(l)) * kLn2;
+    }
+}
+
+hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
+                                int B, int H, int N, float scale, bool causal, hipStream_t stream) {
+    const int BH = B * H;
+    const int nqt = (N + B16_BR - 1) / B16_BR;
+    const long long grid = (long long)nqt * BH;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float c = scale * kLog2e;
+    if (causal)
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)grid), dim3(B16_THREADS), 0, stream,
+                           q, k, v, o, lse, N, BH, nqt, c);
+    else
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)grid), dim3(B16_THREADS), 0, stream,
+                           q, k, v, o, lse, N, BH, nqt, c);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,195 @@
+// attn_fwd_f32.hip - fp32 fused attention forward on the vector ALUs (no MFMA).
+//
+// What it computes is the definition in [FA2-v2 blog] sections 1.3 and 3.3:
+// O = softmax(scale Q K^T) V with an optional causal mask (section 3.4), plus
+// the per-row log-sum-exp.  The structure follows the blog's v2 loop order
+// (section 1.1: query tile outer, key/value tiles inner, one workgroup per
+// (query tile, batch*head)) with these MI355X choices:
+//   * one query row per lane, as in the blog, but the query row and the
+//     unnormalised accumulator live in VGPRs (64 + 64 floats per lane)
+//     instead of shared memory -- the blog's section 4.2 attributes its
+//     remaining stall to the 66KB of Qs+Oacc in shared memory capping
+//     occupancy;
+//   * K/V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
+//     register staging) into a double buffer (the cp.async double buffer of
+//     section 3.2); rows past N are clamped to row N-1 and masked to -inf;
+//   * every lane of a wave reads the same K/V row, so LDS reads are
+//     broadcasts and need no padding (section 3.1 makes the same point);
+//   * the score is kept in the log2 domain (scale * log2(e) folded into Q)
+//     and exponentials use v_exp_f32;
+//   * P is formed as exp2(s - m_new) directly, which equals the blog's
+//     beta * exp(S - m~) and saves one multiply per output element;
+//     a row whose scores in a tile are all masked then contributes exact
+//     zeros (exp2(-inf) = 0), avoiding the NaN of exp(-inf - (-inf)).
+#include "common.h"
+
+namespace mla {
+
+constexpr int F32_D = 64;
+constexpr int F32_BR = 128;  // query rows per workgroup (one per lane)
+constexpr int F32_BC = 32;   // keys per tile
+constexpr int F32_THREADS = F32_BR;
+constexpr int F32_LOADS_PER_WAVE = (F32_BC * F32_D * 4) / (16 * 64) / (F32_THREADS / 64);  // per K (or V) tile
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int N, int BH, int num_q_tiles, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) float Ks[2][F32_BC * F32_D];
+    __shared__ __attribute__((aligned(16))) float Vs[2][F32_BC * F32_D];
+
+    // Work mapping: the id's low part is batch*head, so every (b,h) keeps one
+    // XCD (ids are dealt round-robin over the 8 XCDs and BH is a multiple of
+    // 8 in practice); causal tiles are dealt heaviest first.
+    const int id = blockIdx.x;
+    const int bh = id % BH;
+    const int rank = id / BH;
+    const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+    const int q_start = qt * F32_BR;
+    const size_t base = (size_t)bh * N * F32_D;
+
+    const int tid = threadIdx.x;
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int row = q_start + tid;
+    const bool row_valid = row < N;
+    const int row_c = row_valid ? row : (N - 1);
+
+    // Query row into registers, pre-scaled into the log2 domain.
+    float qr[F32_D];
+    {
+        const float4* qp = reinterpret_cast<const float4*>(q + base + (size_t)row_c * F32_D);
+#pragma unroll
+        for (int i = 0; i < F32_D / 4; ++i) {
+            float4 t = qp[i];
+            qr[4 * i + 0] = t.x * scale_log2;
+            qr[4 * i + 1] = t.y * scale_log2;
+            qr[4 * i + 2] = t.z * scale_log2;
+            qr[4 * i + 3] = t.w * scale_log2;
+        }
+    }
+
+    const int kv_limit = CAUSAL ? min(q_start + F32_BR, N) : N;
+    const int Tc = (kv_limit + F32_BC - 1) / F32_BC;
+
+    // Tile loader: wave w copies chunks [w*L*64, (w+1)*L*64) of 16 bytes of
+    // the K tile and of the V tile (L = loads per wave per tile).
+    auto issue_tile = [&](int j, int buf) {
+        const int kv_start = j * F32_BC;
+#pragma unroll
+        for (int i = 0; i < F32_LOADS_PER_WAVE; ++i) {
+            const int chunk0 = (w * F32_LOADS_PER_WAVE + i) * 64;
+            const int chunk = chunk0 + lane;
+            const int r = chunk / (F32_D / 4);
+            const int c4 = chunk % (F32_D / 4);
+            const int key = min(kv_start + r, N - 1);
+            const size_t goff = base + (size_t)key * F32_D + c4 * 4;
+            gload_lds16(k + goff, &Ks[buf][chunk0 * 4]);
+            gload_lds16(v + goff, &Vs[buf][chunk0 * 4]);
+        }
+    };
+
+    float oacc[F32_D];
+#pragma unroll
+    for (int d = 0; d < F32_D; ++d) oacc[d] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    issue_tile(0, 0);
+    for (int j = 0; j < Tc; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < Tc) {
+            issue_tile(j + 1, buf ^ 1);
+            wait_vmcnt<2 * F32_LOADS_PER_WAVE>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+
+        const int kv_start = j * F32_BC;
+        const float4* Kt = reinterpret_cast<const float4*>(Ks[buf]);
+        const float4* Vt = reinterpret_cast<const float4*>(Vs[buf]);
+
+        float s[F32_BC];
+#pragma unroll
+        for (int c = 0; c < F32_BC; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < F32_D / 4; ++i) {
+                float4 kk = Kt[c * (F32_D / 4) + i];
+                acc = __builtin_fmaf(qr[4 * i + 0], kk.x, acc);
+                acc = __builtin_fmaf(qr[4 * i + 1], kk.y, acc);
+                acc = __builtin_fmaf(qr[4 * i + 2], kk.z, acc);
+                acc = __builtin_fmaf(qr[4 * i + 3], kk.w, acc);
+            }
+            s[c] = acc;
+        }
+        // Masks: keys past N only on the last tile; causal element mask only
+        // on tiles that straddle the diagonal (section 3.4).
+        const bool tail = kv_start + F32_BC > N;
+        const bool diag = CAUSAL && (kv_start + F32_BC - 1 > q_start);
+        if (tail || diag) {
+            const int lim = diag ? min(row_c + 1, N) : N;
+#pragma unroll
+            for (int c = 0; c < F32_BC; ++c)
+                if (kv_start + c >= lim) s[c] = -INFINITY;
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int c = 1; c < F32_BC; ++c) mt = fmaxf(mt, s[c]);
+        const float m_new = fmaxf(m, mt);
+        const float mb = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m - mb);
+        float ls = 0.f;
+#pragma unroll
+        for (int c = 0; c < F32_BC; ++c) {
+            s[c] = fast_exp2(s[c] - mb);
+            ls += s[c];
+        }
+        l = l * alpha + ls;
+        m = m_new;
+#pragma unroll
+        for (int d = 0; d < F32_D; ++d) oacc[d] *= alpha;
+#pragma unroll
+        for (int c = 0; c < F32_BC; ++c) {
+            const float p = s[c];
+#pragma unroll
+            for (int i = 0; i < F32_D / 4; ++i) {
+                float4 vv = Vt[c * (F32_D / 4) + i];
+                oacc[4 * i + 0] = __builtin_fmaf(p, vv.x, oacc[4 * i + 0]);
+                oacc[4 * i + 1] = __builtin_fmaf(p, vv.y, oacc[4 * i + 1]);
+                oacc[4 * i + 2] = __builtin_fmaf(p, vv.z, oacc[4 * i + 2]);
+                oacc[4 * i + 3] = __builtin_fmaf(p, vv.w, oacc[4 * i + 3]);
+            }
+        }
+        lds_barrier();
+    }
+
+    if (row_valid) {
+        const float inv_l = 1.f / l;
+        float4* op = reinterpret_cast<float4*>(o + base + (size_t)row * F32_D);
+#pragma unroll
+        for (int i = 0; i < F32_D / 4; ++i)
+            op[i] = make_float4(oacc[4 * i] * inv_l, oacc[4 * i + 1] * inv_l, oacc[4 * i + 2] * inv_l,
+                                oacc[4 * i + 3] * inv_l);
+        if (lse) lse[(size_t)bh * N + row] = (m + __builtin_log2f(l)) * kLn2;
+    }
+}
+
+// Host-side launcher (called by the C ABI after validation).
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               int B, int H, int N, float scale, bool causal, hipStream_t stream) {
+    const int BH = B * H;
+    const int nqt = (N + F32_BR - 1) / F32_BR;
+    const long long grid = (long long)nqt * BH;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float sl2 = scale * kLog2e;
+    if (causal)
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<true>, dim3((unsigned)grid), dim3(F32_THREADS), 0, stream,
+                           q, k, v, o, lse, N, BH, nqt, sl2);
+    else
+        hipLaunchKernelGGL(attn_fwd_f32_kernel<false>, dim3((unsigned)grid), dim3(F32_THREADS), 0, stream,
+                           q, k, v, o, lse, N, BH, nqt, sl2);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,144 @@
+// common.h - device primitives shared by the gfx950 kernels of libmla_attn.
+//
+// Everything here is CDNA4 (gfx950) specific: wave64, bf16 MFMA with eight
+// bf16 per lane (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_32x32x16_bf16), the
+// transposing LDS read ds_read_b64_tr_b16, direct global->LDS loads
+// (global_load_lds_dwordx4), and v_permlane16/32_swap for cross-row
+// exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+#define MLA_GLOBAL __attribute__((address_space(1)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// MFMA.  Operand layouts (verified on the device):
+//  16x16x32: A lane l holds row l%16, k = 8*(l/16)+[0..7];
+//            B lane l holds col l%16, k = 8*(l/16)+[0..7];
+//            D lane l holds col l%16, rows 4*(l/16)+[0..3].
+//  32x32x16: A lane l holds row l%32, k = 8*(l/32)+[0..7];
+//            B lane l holds col l%32, k = 8*(l/32)+[0..7];
+//            D register v of lane l: col l%32, row 8*(v/4)+4*(l/32)+v%4.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// LDS helpers
+// ---------------------------------------------------------------------------
+// 16-byte LDS read at a byte offset from an LDS base.
+__device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t byte_off) {
+    return *reinterpret_cast<const bf16x8*>(base + byte_off);
+}
+
+// ds_read_b64_tr_b16.  Within each group of 16 lanes, lane s supplies the
+// address of four consecutive 16-bit elements; result lane i, element j is
+// element i%4 of the chunk addressed by lane 4*j + i/4 of the same group.
+// Used to fetch a B (or A) MFMA operand whose contraction index runs down
+// the rows of a row-major tile: if lane s = 4*j + q of a group points at
+// row (r0 + j), columns (c0 + 4q .. c0 + 4q + 3), lane i receives
+// rows r0..r0+3 of column c0 + i.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* base, uint32_t byte_off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 MLA_LDS*)((MLA_LDS char*)(base) + byte_off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane.  The wave's 64 chunks land
+// contiguously at lds_wave_base + 16 * lane, whatever global address each
+// lane supplies (lane order fixes the LDS position).
+__device__ __forceinline__ void gload_lds16(const void* gsrc, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const void MLA_GLOBAL*)gsrc,
+                                     (void MLA_LDS*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions
+// ---------------------------------------------------------------------------
+// Max / sum over the four lanes {l, l^16, l^32, l^48} (the four row groups
+// of a 16x16 MFMA result).  v_permlane16_swap exchanges lanes l and l^16
+// (within each 32-lane half), v_permlane32_swap exchanges l and l^32; each
+// returns the pair (own, partner) in some order.
+__device__ __forceinline__ float max4_groups16(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    u = __float_as_uint(x);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum4_groups16(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    u = __float_as_uint(x);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// Max / sum over lanes {l, l^32} (the two row groups of a 32x32 result).
+__device__ __forceinline__ float max2_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum2_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Workgroup barrier for LDS hand-offs in the tile loops.  The wave's own
+// direct-to-LDS copies are waited for explicitly (wait_vmcnt) before it, and
+// its LDS reads are drained here (lgkmcnt 0), so no memory fence -- which
+// would also drain the next tile's in-flight copies -- is needed.  The empty
+// asm statements stop the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace mla

@@ -1,0 +1,97 @@
+// mla_absorb.hip - weight-absorption prologue q_lat = q_nope W_UK (gfx950).
+//
+// [MLA-FA3 article] section 2: the key up-projection W_UK is absorbed into
+// the query, so the score against the cache needs (q W_UK) once per query
+// instead of W_UK c once per cached token.  This kernel forms
+//   q_lat[b, h, :] = q_nope[b, h, :] @ W_UK[h]     (fp32 accumulation, bf16 out)
+// for all b, h.  It is a per-head batched product (M = B, N = Dl, K = Dn);
+// at the decode shapes it moves ~59 MB for ~4 GFLOP, so it is bound by
+// memory, and the design only has to read W_UK once and stream q_nope.
+//
+// A workgroup owns (head h, 128 latent columns): it copies that
+// [Dn x 128] slab of W_UK into LDS once, then walks all b in blocks of 64
+// (16 per wave).  The product is taken transposed, q_lat^T = W^T q_nope^T
+// (v_mfma_f32_16x16x32_bf16): A = W^T fragments read with ds_read_b64_tr_b16
+// from the row-major slab, B = q_nope rows read straight from global memory
+// (16 contiguous bytes per lane), so each lane ends with 4 consecutive
+// latent columns of one row and stores them as 8 bytes.
+#include "common.h"
+
+namespace mla {
+
+constexpr int ABS_THREADS = 256;
+constexpr int ABS_COLS = 128;
+
+__device__ __forceinline__ int abs_swz(int r) { return (r & 7) << 1; }
+
+__global__ __launch_bounds__(ABS_THREADS, 2) void mla_absorb_kernel(const __bf16* __restrict__ q_nope,
+                                                                   const __bf16* __restrict__ w_uk,
+                                                                   __bf16* __restrict__ q_lat, int B, int H,
+                                                                   int Dn, int Dl) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // [Dn][128] bf16, 256-byte rows
+    const int h = blockIdx.y;
+    const int col0 = blockIdx.x * ABS_COLS;
+    const int w = wave_id();
+    const int lane = lane_id();
+
+    // W_UK[h][:, col0:col0+128] -> LDS, chunk p of row r stored at p ^ abs_swz(r).
+    {
+        const __bf16* src = w_uk + (size_t)h * Dn * Dl + col0;
+        const int chunks = Dn * 16;
+        for (int c0 = w * 64; c0 < chunks; c0 += 4 * 64) {
+            const int L = c0 + lane;
+            const int r = L >> 4, p = L & 15;
+            gload_lds16(src + (size_t)r * Dl + 8 * (p ^ abs_swz(r)), smem + c0 * 16);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    const int n = lane & 15, g = lane >> 4;
+    const int jj = n >> 2, qd = n & 3;
+    for (int bb = 0; bb < B; bb += 64) {
+        const int b = bb + 16 * w + n;
+        const int bl = min(b, B - 1);
+        const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)bl * H + h) * Dn);
+        f32x4 acc[ABS_COLS / 16];
+#pragma unroll
+        for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < Dn / 32; ++kk) {
+            const bf16x8 bq = qrow[4 * kk + g];
+            const int r_lo = 32 * kk + 8 * g + jj, r_hi = r_lo + 4;
+#pragma unroll
+            for (int db = 0; db < ABS_COLS / 16; ++db) {
+                const int ch = 2 * db + (qd >> 1), half = (qd & 1) * 8;
+                bf16x4 lo = lds_read_tr16(smem, r_lo * 256 + ((ch ^ abs_swz(r_lo)) << 4) + half);
+                bf16x4 hi = lds_read_tr16(smem, r_hi * 256 + ((ch ^ abs_swz(r_hi)) << 4) + half);
+                acc[db] = mfma16(join(lo, hi), bq, acc[db]);
+            }
+        }
+        if (b < B) {
+            __bf16* out = q_lat + ((size_t)b * H + h) * Dl + col0;
+#pragma unroll
+            for (int db = 0; db < ABS_COLS / 16; ++db) {
+                bf16x4 t;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[db][r]);
+                *reinterpret_cast<bf16x4*>(out + 16 * db + 4 * g) = t;
+            }
+        }
+    }
+}
+
+hipError_t ensure_smem_attr(const void* fn, int bytes);
+
+hipError_t launch_mla_absorb(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
+                             hipStream_t stream) {
+    const int smem = Dn * ABS_COLS * 2;
+    if (smem > 64 * 1024) {
+        hipError_t e = ensure_smem_attr((const void*)mla_absorb_kernel, smem);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(mla_absorb_kernel, dim3(Dl / ABS_COLS, H), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
+                       q_lat, B, H, Dn, Dl);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,519 @@
+// mla_decode.hip - absorbed MLA decode over the latent KV cache (gfx950).
+//
+// [MLA-FA3 article]: each cached token is one 576-wide bf16 row, the 512-dim
+// compressed latent c^KV followed by the 64-dim decoupled RoPE key k^R
+// (section 1 packs both into one descriptor row of latent_dim = 576).  With
+// W_UK absorbed into the query (section 2, absorption equation) a head's
+// score is one 576-wide dot product [q_lat || q_rope] . row, and the output
+// is the softmax-weighted sum of the rows' first 512 dims.  The article's
+// fused dataflow streams cache tiles on chip, takes both dot products there,
+// applies online-softmax scaling with a partial reduction, accumulates in
+// fp32 registers, and never writes a decompressed key or value.
+//
+// Three kernels run in stream order:
+//   1. mla_plan_kernel   (one workgroup): split plan from seqlens.
+//   2. mla_split_kernel  (one workgroup per part x 128-head block): streams
+//      the part's cache tiles through LDS and writes either the final output
+//      (sequence handled by one part) or an fp32 partial (o_s, lse_s).
+//   3. mla_combine_slots_kernel: log-sum-exp merge of the partials of every
+//      split sequence; also writes o = 0, lse = -inf for empty sequences.
+//
+// Split-kernel tiling.  A workgroup has 4 waves (one per SIMD); wave w owns
+// 32 heads, so the workgroup serves 128 heads and every cache byte crosses
+// HBM -> LDS once for all of them.  Per wave the state is the q fragments
+// (32 heads x 576 bf16 = 144 VGPRs) and the fp32 output accumulator
+// (32 heads x 512 = 256 registers), which needs the full 512-entry register
+// file of a single wave per SIMD.  A 64-token tile (64 x 1152 B = 72 KiB) is
+// copied global -> LDS with global_load_lds_dwordx4 into one of two buffers
+// (147,456 B of LDS).  Per 32-token block and wave
+// (v_mfma_f32_32x32x16_bf16):
+//   S^T = C q^T   A = cache rows from LDS (K = 576 = 36 steps), B = the
+//                 wave's q fragments.  Rows are fed in a permuted order so
+//                 that lane (head, g) ends with tokens 16ks+8g..+7 of each
+//                 16-token k-step in consecutive registers.
+//   O^T += C^T P^T  A = latent columns read transposed with
+//                 ds_read_b64_tr_b16 from the same LDS tile, B = P in bf16.
+// The same LDS bytes serve as key (576 dims) and value (first 512 dims).
+#include <atomic>
+
+#include "common.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+constexpr int DEC_WAVES = 8;
+constexpr int DEC_HEADS = 16;  // heads per wave
+constexpr int DEC_THREADS = DEC_WAVES * 64;
+static_assert(DEC_WAVES * DEC_HEADS == kDecodeHeadsPerWG, "head split");
+constexpr int DEC_ROW_CHUNKS = kRow * 2 / 16;                     // 72 chunks of 16 B per token
+constexpr int DEC_STRIDE_CHUNKS = DEC_ROW_CHUNKS + 1;             // +1 pad chunk per row in LDS
+constexpr int DEC_ROW_STRIDE = DEC_STRIDE_CHUNKS * 16;            // 1168 B (== 16 mod 128)
+constexpr int DEC_TILE_BYTES = kDecodeTile * DEC_ROW_STRIDE;      // 74752
+constexpr int DEC_TILE_INSTR = kDecodeTile * DEC_STRIDE_CHUNKS / 64;  // 73 wave-wide 1 KiB copies
+constexpr int DEC_SMEM = 2 * DEC_TILE_BYTES;                      // 149504
+static_assert(kDecodeTile * DEC_STRIDE_CHUNKS % 64 == 0, "whole copies");
+static_assert(DEC_SMEM <= 160 * 1024, "LDS");
+constexpr int DEC_LOADS_HI = (DEC_TILE_INSTR + DEC_WAVES - 1) / DEC_WAVES;  // copies issued by wave 0
+constexpr int DEC_LOADS_LO = DEC_TILE_INSTR / DEC_WAVES;                    // by the other waves
+static_assert(DEC_TILE_INSTR % DEC_WAVES == 1, "wave 0 issues the one extra copy");
+constexpr int DEC_PF = 2;  // LDS fragment prefetch distance, in MFMA steps
+
+struct PlanArgs {
+    int seq_len, seq_n, seq_start, seq_first, seq_nsplit, part_first_seq;  // int32 offsets
+    long long o_part_off, lse_part_off;                                    // byte offsets
+};
+
+// LDS layout of a tile: token row r at byte r * 1168 (72 data chunks + 1
+// pad chunk).  With a row stride of 16 (mod 128) bytes, eight rows whose
+// indices differ in their low three bits fall on distinct 16-byte bank
+// groups, and four rows two apart (the transposed reads below) fall on
+// distinct 32-byte groups.
+
+// ---------------------------------------------------------------------------
+// 1. Plan.  Cost line: sequence b occupies n_b + c0 positions (n_b tiles
+//    after c0 positions of fixed cost), empty sequences occupy none; part p
+//    owns positions [p t, (p+1) t) with
+//      t = max(ceil(C / parts), ceil(max_n / (num_splits - 1)), t_min, 1),
+//    which bounds every sequence to at most num_splits parts.  With
+//    num_splits == 1 each sequence gets its own part (t = max_n + c0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ seqlens, int* __restrict__ ws,
+                                                       int B, int S_max, int parts, int c0, int t_min,
+                                                       int num_splits, PlanArgs a) {
+    __shared__ int scan[1024];
+    __shared__ int s_max, s_clamp, s_carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_max = 0; s_clamp = 0; s_carry = 0; }
+    __syncthreads();
+    for (int base = 0; base < B; base += 1024) {
+        const int b = base + tid;
+        int cost = 0;
+        if (b < B) {
+            const int raw = seqlens[b];
+            const int len = min(max(raw, 0), S_max);
+            if (len != raw) atomicAdd(&s_clamp, 1);
+            const int n = (len + kDecodeTile - 1) / kDecodeTile;
+            cost = n > 0 ? n + c0 : 0;
+            ws[a.seq_len + b] = len;
+            ws[a.seq_n + b] = n;
+            atomicMax(&s_max, n);
+        }
+        scan[tid] = cost;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int add = tid >= d ? scan[tid - d] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        if (b < B) ws[a.seq_start + b] = s_carry + scan[tid] - cost + c0;
+        __syncthreads();
+        if (tid == 0) s_carry += scan[1023];
+        __syncthreads();
+    }
+    const int max_n = s_max;
+    const bool whole = num_splits == 1;
+    int t, C, parts_used, nparts;
+    if (whole) {
+        t = max(max_n + c0, 1);
+        C = B * t;
+        parts_used = B;
+        nparts = B;
+    } else {
+        C = s_carry;
+        t = max(max((C + parts - 1) / parts, (max_n + num_splits - 2) / (num_splits - 1)), max(t_min, 1));
+        parts_used = (C + t - 1) / t;
+        nparts = parts;
+    }
+    for (int p = tid; p < nparts; p += 1024) ws[a.part_first_seq + p] = B;
+    __syncthreads();
+    for (int b = tid; b < B; b += 1024) {
+        const int n = ws[a.seq_n + b];
+        int start = ws[a.seq_start + b];
+        if (whole) {
+            start = b * t + c0;
+            ws[a.seq_start + b] = start;
+        }
+        const int first = n > 0 ? start / t : 0;
+        const int ns = n > 0 ? (start + n - 1) / t - first + 1 : 0;
+        ws[a.seq_first + b] = first;
+        ws[a.seq_nsplit + b] = ns;
+        for (int p = first; p < first + ns; ++p) atomicMin(&ws[a.part_first_seq + p], b);
+    }
+    if (tid == 0) {
+        ws[kHdrPartsUsed] = parts_used;
+        ws[kHdrT] = t;
+        ws[kHdrC] = C;
+        ws[kHdrTile] = kDecodeTile;
+        ws[kHdrC0] = c0;
+        ws[kHdrMode] = whole ? 1 : 0;
+        ws[kHdrParts] = nparts;
+        ws[kHdrClamped] = s_clamp;
+        ws[kHdrMaxN] = max_n;
+        ws[kHdrB] = B;
+        ws[kHdrTMin] = t_min;
+        ws[kHdrNumSplits] = num_splits;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. Split kernel
+// ---------------------------------------------------------------------------
+struct DecodeCtx {
+    const __bf16* q_lat;
+    const __bf16* q_rope;
+    const __bf16* cache;
+    const int* ws;
+    float* o_part;
+    float* lse_part;
+    __bf16* o;
+    float* lse;
+    int H, S_max;
+    float c_log2;
+    PlanArgs a;
+};
+
+// Copy one 64-token tile to LDS: copy i (0..72) of 64 chunks is issued by
+// wave i % 4.  Chunk L of the tile is row L / 73, chunk L % 73 of that row;
+// the pad chunk (72) receives a second copy of chunk 0.  Rows past the
+// sequence end repeat its last token (finite data; their scores are masked).
+__device__ __forceinline__ void dec_issue_tile(const DecodeCtx& x, char* buf, int b, int tok0, int len, int w,
+                                               int lane) {
+    const __bf16* seq = x.cache + (size_t)b * x.S_max * kRow;
+    for (int i = w; i < DEC_TILE_INSTR; i += DEC_WAVES) {
+        const int L = i * 64 + lane;
+        const int r = L / DEC_STRIDE_CHUNKS;
+        int c = L - r * DEC_STRIDE_CHUNKS;
+        c = (c == DEC_ROW_CHUNKS) ? 0 : c;
+        const int tok = min(tok0 + r, len - 1);
+        gload_lds16(seq + (size_t)tok * kRow + 8 * c, buf + i * 1024);
+    }
+}
+
+__device__ __forceinline__ void dec_wait_prev_tile(int w) {
+    if (w == 0) wait_vmcnt<DEC_LOADS_HI>();
+    else wait_vmcnt<DEC_LOADS_LO>();
+}
+
+// Token permutation inside a 32-token block, for v_mfma_f32_16x16x32_bf16.
+// The two S^T = C q^T products of a block (tokens 0..15 and 16..31) feed
+// MFMA row i = 4g + j the token pi(i) = 2j + (g & 1) + 8(g >> 1) (+16 for the
+// second).  Lane group g of the results then holds, in its eight registers
+// (four per product), the tokens that the P^T operand of the PV product
+// assigns to logical k = 8g + e, and:
+//  * the 8 rows an 8-lane group reads for S^T have distinct low 3 bits
+//    (distinct 16-byte bank groups with the 1168-byte row stride);
+//  * the 4 rows a 16-lane ds_read_b64_tr_b16 touches are two apart
+//    (distinct 32-byte bank groups).
+__device__ __forceinline__ int dec_pi16(int i) { return 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3); }
+__device__ __forceinline__ int dec_token_of(int g, int e) {  // e = 0..7 of lane group g
+    return 16 * (e >> 2) + 2 * (e & 3) + (g & 1) + 8 * (g >> 1);
+}
+
+__device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile_lo, int tile_hi) {
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int n = lane & 15;  // head column of the MFMA results / MFMA row of the A operand
+    const int g = lane >> 4;  // row group (0..3)
+    const int H = x.H;
+    const int hbase = blockIdx.y * kDecodeHeadsPerWG + DEC_HEADS * w;
+    const bool active = hbase < H;  // H % 16 == 0: a wave is fully in or out
+    const int head = hbase + n;
+    const int len = x.ws[x.a.seq_len + b];
+    const int tok_end = min(tile_hi * kDecodeTile, len);
+
+    // q as the B operand of S^T = C q^T: lane (head n, g) holds dims 32kk+8g..+7.
+    bf16x8 qf[kRow / 32];
+    if (active) {
+        const bf16x8* ql = reinterpret_cast<const bf16x8*>(x.q_lat + ((size_t)b * H + head) * kLatent);
+        const bf16x8* qr = reinterpret_cast<const bf16x8*>(x.q_rope + ((size_t)b * H + head) * kRope);
+#pragma unroll
+        for (int kk = 0; kk < kLatent / 32; ++kk) qf[kk] = ql[4 * kk + g];
+#pragma unroll
+        for (int kk = 0; kk < kRope / 32; ++kk) qf[kLatent / 32 + kk] = qr[4 * kk + g];
+    }
+
+    f32x4 oacc[kLatent / 16];
+#pragma unroll
+    for (int db = 0; db < kLatent / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    // Per-lane LDS byte offsets; everything else is a compile-time immediate.
+    const int qk_off = dec_pi16(n) * DEC_ROW_STRIDE + 16 * g;
+    const int jj = n >> 2, qd = n & 3;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
+    const int pv_off = dec_pi16(4 * g + jj) * DEC_ROW_STRIDE + 8 * qd;
+    const int ntiles = tile_hi - tile_lo;
+
+    dec_issue_tile(x, smem, b, tile_lo * kDecodeTile, len, w, lane);
+    for (int j = 0; j < ntiles; ++j) {
+        char* cur = smem + (j & 1) * DEC_TILE_BYTES;
+        if (j + 1 < ntiles) {
+            dec_issue_tile(x, smem + ((j + 1) & 1) * DEC_TILE_BYTES, b, (tile_lo + j + 1) * kDecodeTile, len, w,
+                           lane);
+            dec_wait_prev_tile(w);
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        if (active) {
+            const int valid = tok_end - (tile_lo + j) * kDecodeTile;  // >= 1
+#pragma unroll
+            for (int tb = 0; tb < kDecodeTile / 32; ++tb) {
+                // ---- scores for tokens 32tb..32tb+31: sa (first 16), sb (second 16) ----
+                const char* qk_base = cur + qk_off + 32 * tb * DEC_ROW_STRIDE;
+                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+                {
+                    // Fragment reads run DEC_PF steps ahead of the MFMAs that
+                    // consume them; schedule barriers keep the compiler from
+                    // hoisting every read (which would exhaust the VGPRs).
+                    constexpr int KS = kRow / 32;
+                    bf16x8 fa[DEC_PF + 1], fb[DEC_PF + 1];
+#pragma unroll
+                    for (int i = 0; i < DEC_PF; ++i) {
+                        fa[i] = lds_read16(qk_base, 64 * i);
+                        fb[i] = lds_read16(qk_base, 16 * DEC_ROW_STRIDE + 64 * i);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) {
+                        if (kk + DEC_PF < KS) {
+                            fa[(kk + DEC_PF) % (DEC_PF + 1)] = lds_read16(qk_base, 64 * (kk + DEC_PF));
+                            fb[(kk + DEC_PF) % (DEC_PF + 1)] =
+                                lds_read16(qk_base, 16 * DEC_ROW_STRIDE + 64 * (kk + DEC_PF));
+                        }
+                        sa = mfma16(fa[kk % (DEC_PF + 1)], qf[kk], sa);
+                        sb = mfma16(fb[kk % (DEC_PF + 1)], qf[kk], sb);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                if (valid < 32 * tb + 32) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (32 * tb + dec_token_of(g, r) >= valid) sa[r] = -INFINITY;
+                        if (32 * tb + dec_token_of(g, 4 + r) >= valid) sb[r] = -INFINITY;
+                    }
+                }
+                // ---- online softmax (log2 domain) ----
+                float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                                 fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+                mt = max4_groups16(mt) * x.c_log2;
+                const float m_new = fmaxf(m, mt);
+                const float mb = (m_new == -INFINITY) ? 0.f : m_new;
+                if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+                    const float alpha = fast_exp2(m - mb);
+                    l *= alpha;
+#pragma unroll
+                    for (int db = 0; db < kLatent / 16; ++db) oacc[db] *= alpha;
+                }
+                m = m_new;
+                bf16x8 pb;  // logical k = 8g + e
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pa = fast_exp2(__builtin_fmaf(sa[r], x.c_log2, -mb));
+                    const float pq = fast_exp2(__builtin_fmaf(sb[r], x.c_log2, -mb));
+                    l += pa + pq;
+                    pb[r] = to_bf16(pa);
+                    pb[4 + r] = to_bf16(pq);
+                }
+                // ---- O^T += C^T P^T over the 512 latent dims ----
+                {
+                    const char* pv_base = cur + pv_off + 32 * tb * DEC_ROW_STRIDE;
+                    constexpr int NS = kLatent / 16;
+                    auto rd = [&](int db) {
+                        return join(lds_read_tr16(pv_base, 32 * db),
+                                    lds_read_tr16(pv_base, 16 * DEC_ROW_STRIDE + 32 * db));
+                    };
+                    bf16x8 fv[DEC_PF + 1];
+#pragma unroll
+                    for (int i = 0; i < DEC_PF; ++i) fv[i] = rd(i);
+#pragma unroll
+                    for (int db = 0; db < NS; ++db) {
+                        if (db + DEC_PF < NS) fv[(db + DEC_PF) % (DEC_PF + 1)] = rd(db + DEC_PF);
+                        oacc[db] = mfma16(fv[db % (DEC_PF + 1)], pb, oacc[db]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    }
+
+    if (!active) return;
+    l = sum4_groups16(l);
+    const float inv_l = 1.f / l;
+    const float lse_v = (m + __builtin_log2f(l)) * kLn2;
+    // O^T block db: lane (head n, g) holds dims 16db + 4g + 0..3.
+    const int ns = x.ws[x.a.seq_nsplit + b];
+    if (ns == 1) {
+        __bf16* op = x.o + ((size_t)b * H + head) * kLatent + 4 * g;
+#pragma unroll
+        for (int db = 0; db < kLatent / 16; ++db) {
+            bf16x4 t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][r] * inv_l);
+            *reinterpret_cast<bf16x4*>(op + 16 * db) = t;
+        }
+        if (x.lse && g == 0) x.lse[(size_t)b * H + head] = lse_v;
+    } else {
+        const int slot = 2 * p + (x.ws[x.a.part_first_seq + p] == b ? 0 : 1);
+        float* op = x.o_part + ((size_t)slot * H + head) * kLatent + 4 * g;
+#pragma unroll
+        for (int db = 0; db < kLatent / 16; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = oacc[db] * inv_l;
+        if (g == 0) x.lse_part[(size_t)slot * H + head] = lse_v;
+    }
+}
+
+__global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int p = blockIdx.x;
+    const int* ws = x.ws;
+    const int parts_used = ws[kHdrPartsUsed];
+    if (p >= parts_used) return;
+    const int t = ws[kHdrT];
+    const int whole = ws[kHdrMode];
+    const int B = ws[kHdrB];
+    const int pos_lo = p * t, pos_hi = pos_lo + t;
+    for (int b = ws[x.a.part_first_seq + p]; b < B; ++b) {
+        const int nb = ws[x.a.seq_n + b];
+        const int sb = ws[x.a.seq_start + b];
+        if (nb > 0) {
+            if (sb >= pos_hi) break;
+            const int lo = max(sb, pos_lo) - sb;
+            const int hi = min(sb + nb, pos_hi) - sb;
+            if (lo < hi) dec_piece(x, smem, p, b, lo, hi);
+        }
+        if (whole) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Combine: lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.
+//    Empty splits (lse_s = -inf) weigh 0; all empty -> o = 0, lse = -inf.
+// ---------------------------------------------------------------------------
+template <typename SlotFn>
+__device__ __forceinline__ void combine_row(const float* o_part, const float* lse_part, size_t row_stride_o,
+                                            int nsplit, SlotFn slot_of, __bf16* o_row, float* lse_out, int d4) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse_part[slot_of(s)]);
+    if (M == -INFINITY) {
+        *reinterpret_cast<bf16x4*>(o_row + 4 * d4) = bf16x4{to_bf16(0.f), to_bf16(0.f), to_bf16(0.f), to_bf16(0.f)};
+        if (lse_out && d4 == 0) *lse_out = -INFINITY;
+        return;
+    }
+    float W = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+        const size_t sl = slot_of(s);
+        const float ls = lse_part[sl];
+        const float wgt = (ls == -INFINITY) ? 0.f : __expf(ls - M);
+        W += wgt;
+        if (wgt != 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(o_part + sl * row_stride_o + 4 * d4);
+    }
+    const float inv = 1.f / W;
+    bf16x4 t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[r] * inv);
+    *reinterpret_cast<bf16x4*>(o_row + 4 * d4) = t;
+    if (lse_out && d4 == 0) *lse_out = M + __logf(W);
+}
+
+// Partials of the split kernel: slot-major [slots][H][512].
+__global__ __launch_bounds__(256) void mla_combine_slots_kernel(const int* __restrict__ ws, const float* o_part,
+                                                               const float* lse_part, __bf16* o, float* lse,
+                                                               int H, PlanArgs a) {
+    const int b = blockIdx.x;
+    const int ns = ws[a.seq_nsplit + b];
+    if (ns == 1) return;
+    const int first = ws[a.seq_first + b];
+    const int d4 = threadIdx.x & 127;
+    const int* pfs = ws + a.part_first_seq;
+    for (int hh = blockIdx.y * 16 + (threadIdx.x >> 7); hh < min(H, (int)(blockIdx.y + 1) * 16); hh += 2) {
+        __bf16* orow = o + ((size_t)b * H + hh) * kLatent;
+        float* lrow = lse ? lse + (size_t)b * H + hh : nullptr;
+        auto slot_of = [&](int s) -> size_t {
+            const int p = first + s;
+            const int slot = 2 * p + (pfs[p] == b ? 0 : 1);
+            return (size_t)slot * H + hh;
+        };
+        // row index = slot*H + hh, so o_part row stride is kLatent floats
+        combine_row(o_part, lse_part, kLatent, ns, slot_of, orow, lrow, d4);
+    }
+}
+
+// Caller-supplied dense partials: o_part [B,H,S,512], lse_part [B,H,S].
+__global__ __launch_bounds__(256) void mla_combine_dense_kernel(const float* o_part, const float* lse_part,
+                                                               __bf16* o, float* lse, int H, int S) {
+    const int b = blockIdx.x;
+    const int d4 = threadIdx.x & 127;
+    for (int hh = blockIdx.y * 16 + (threadIdx.x >> 7); hh < min(H, (int)(blockIdx.y + 1) * 16); hh += 2) {
+        const size_t row0 = ((size_t)b * H + hh) * S;
+        auto slot_of = [&](int s) -> size_t { return row0 + s; };
+        combine_row(o_part, lse_part, kLatent, S, slot_of, o + ((size_t)b * H + hh) * kLatent,
+                    lse ? lse + (size_t)b * H + hh : nullptr, d4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+// Opt a kernel into more than 64 KiB of dynamic LDS, once per device.
+hipError_t ensure_smem_attr(const void* fn, int bytes) {
+    static std::atomic<int> done[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(bytes, std::memory_order_release);
+    return e;
+}
+
+static PlanArgs plan_args(const PlanLayout& L) {
+    PlanArgs a;
+    a.seq_len = (int)L.seq_len;
+    a.seq_n = (int)L.seq_n;
+    a.seq_start = (int)L.seq_start;
+    a.seq_first = (int)L.seq_first;
+    a.seq_nsplit = (int)L.seq_nsplit;
+    a.part_first_seq = (int)L.part_first_seq;
+    a.o_part_off = (long long)L.o_part_bytes_off;
+    a.lse_part_off = (long long)L.lse_part_bytes_off;
+    return a;
+}
+
+hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __bf16* cache, const int* seqlens,
+                             __bf16* o, float* lse, int B, int H, int S_max, float scale, int num_splits,
+                             const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream) {
+    hipError_t e = ensure_smem_attr((const void*)mla_split_kernel, DEC_SMEM);
+    if (e != hipSuccess) return e;
+    int* ws = static_cast<int*>(workspace);
+    const PlanArgs a = plan_args(L);
+    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, seqlens, ws, B, S_max, L.parts, c0, t_min,
+                       num_splits, a);
+    DecodeCtx x;
+    x.q_lat = q_lat;
+    x.q_rope = q_rope;
+    x.cache = cache;
+    x.ws = ws;
+    x.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_part_bytes_off);
+    x.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_part_bytes_off);
+    x.o = o;
+    x.lse = lse;
+    x.H = H;
+    x.S_max = S_max;
+    x.c_log2 = scale * kLog2e;
+    x.a = a;
+    const int hblocks = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
+    hipLaunchKernelGGL(mla_split_kernel, dim3(L.parts, hblocks), dim3(DEC_THREADS), DEC_SMEM, stream, x);
+    hipLaunchKernelGGL(mla_combine_slots_kernel, dim3(B, (H + 15) / 16), dim3(256), 0, stream, ws, x.o_part,
+                       x.lse_part, o, lse, H, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mla_combine(const float* o_part, const float* lse_part, __bf16* o, float* lse, int B, int H,
+                              int S, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_combine_dense_kernel, dim3(B, (H + 15) / 16), dim3(256), 0, stream, o_part, lse_part, o,
+                       lse, H, S);
+    return hipGetLastError();
+}
+
+}  // namespace mla

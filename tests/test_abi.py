@@ -1,0 +1,118 @@
+"""The C ABI: the library loads, exports every function include/mla_attn.h
+declares, and rejects bad arguments on the host before touching a device.
+No compute call is made here (these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_declares_the_expected_api():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        txt = lib.mla_status_string(s).decode()
+        assert txt.startswith("MLA_"), txt
+    assert lib.mla_status_string(99).decode() == "unknown mla_status_t"
+
+
+P = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+BAD = 0x10008        # misaligned
+
+
+def _attn(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, D=64, scale=0.125, causal=0, dt=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, dt, None)
+
+
+def test_attn_validation_codes(lib):
+    assert _attn(lib, q=None) == binding.MLA_ERR_NULL
+    assert _attn(lib, o=None) == binding.MLA_ERR_NULL
+    assert _attn(lib, B=0) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, N=-1) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, N=(1 << 20) + 1) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, scale=0.0) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, scale=float("nan")) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, causal=2) == binding.MLA_ERR_SHAPE
+    assert _attn(lib, D=128, dt=0) == binding.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, D=64, dt=1) == binding.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, dt=7) == binding.MLA_ERR_UNSUPPORTED
+    assert _attn(lib, k=BAD) == binding.MLA_ERR_ALIGN
+    assert _attn(lib, lse=BAD) == binding.MLA_ERR_ALIGN
+    assert _attn(lib, N=0) == binding.MLA_OK        # nothing to do, nothing enqueued
+
+
+def _dec(lib, ql=P, qr=P, c=P, sl=P, o=P, lse=P, B=2, H=128, S=64, scale=0.04, ns=4, ws=P, wsb=1 << 30):
+    return lib.mla_decode_fwd(ql, qr, c, sl, o, lse, B, H, S, scale, ns, ws, wsb, None)
+
+
+def test_decode_validation_codes(lib):
+    assert _dec(lib, c=None) == binding.MLA_ERR_NULL
+    assert _dec(lib, sl=None) == binding.MLA_ERR_NULL
+    assert _dec(lib, H=8) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, H=40) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, ns=0) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, ns=33) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, S=0) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, B=(1 << 16) + 1) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, B=4096, S=4096) == binding.MLA_ERR_SHAPE   # B*S_max*576 beyond int32 rows
+    assert _dec(lib, scale=-1.0) == binding.MLA_ERR_SHAPE
+    assert _dec(lib, ql=BAD) == binding.MLA_ERR_ALIGN
+    assert _dec(lib, ws=None) == binding.MLA_ERR_WORKSPACE
+
+
+def test_combine_and_absorb_validation_codes(lib):
+    assert lib.mla_combine(None, P, P, P, 1, 1, 2, None) == binding.MLA_ERR_NULL
+    assert lib.mla_combine(P, P, P, P, 1, 1, 0, None) == binding.MLA_ERR_SHAPE
+    assert lib.mla_combine(P, P, P, P, 1, 1, 33, None) == binding.MLA_ERR_SHAPE
+    assert lib.mla_combine(P, BAD, P, P, 1, 1, 2, None) == binding.MLA_ERR_ALIGN
+    assert lib.mla_absorb_q(P, None, P, 4, 8, 128, 512, None) == binding.MLA_ERR_NULL
+    assert lib.mla_absorb_q(P, P, P, 0, 8, 128, 512, None) == binding.MLA_ERR_SHAPE
+    assert lib.mla_absorb_q(P, P, P, 4, 8, 100, 512, None) == binding.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(P, P, P, 4, 8, 128, 500, None) == binding.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(BAD, P, P, 4, 8, 128, 512, None) == binding.MLA_ERR_ALIGN
+
+
+def test_workspace_size_rejects_bad_shapes(lib):
+    assert lib.mla_decode_workspace_size(0, 128, 4) == 0
+    assert lib.mla_decode_workspace_size(4, 17, 4) == 0
+    assert lib.mla_decode_workspace_size(4, 128, 40) == 0
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="would launch with fake pointers on a real device")
+def test_valid_call_without_device_reports_hip_error(lib):
+    # Validation passes; the HIP runtime then reports that there is no device.
+    assert _attn(lib) == binding.MLA_ERR_HIP
+    assert _dec(lib) == binding.MLA_ERR_HIP
+    assert lib.mla_decode_workspace_size(4, 128, 4) == 0

@@ -1,0 +1,187 @@
+"""GPU parity of the MLA decode path (plan + split + combine), the standalone
+LSE combine and the absorption prologue, against the fp64 oracle, through
+the C ABI."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_attn_amd import binding, workloads
+from oracle import mla as OM
+from oracle.plan import plan_pieces_ref, plan_ref
+from tests.gpu_util import check_bf16, check_lse, np64, say, sync
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SCALE = 1 / math.sqrt(576)
+
+
+def decode(d, num_splits):
+    ql, qr, c = d["q_lat"].to(DEV), d["q_rope"].to(DEV), d["cache"].to(DEV)
+    sl = d["seqlens"].to(DEV)
+    B, H, _ = ql.shape
+    ws = binding.alloc_decode_workspace(B, H, num_splits, DEV)
+    o, l = binding.mla_decode_fwd(ql, qr, c, sl, SCALE, num_splits, workspace=ws)
+    sync()
+    return o, l, ws
+
+
+def oracle_decode(d, idx=None):
+    lens = d["seqlens"].tolist()
+    if idx is None:
+        idx = list(range(len(lens)))
+    ql = np64(d["q_lat"][idx])
+    qr = np64(d["q_rope"][idx])
+    Lmax = max(1, max(lens[i] for i in idx))
+    c = np64(d["cache"][idx, :Lmax])
+    return OM.mla_decode_ref(ql, qr, c, [lens[i] for i in idx], SCALE)
+
+
+def check_plan(ws, d, num_splits):
+    B = d["q_lat"].shape[0]
+    got = binding.read_plan(ws, B)
+    ref = plan_ref(d["seqlens"].tolist(), got["tile"], got["parts"] if got["mode"] == "line" else B,
+                   num_splits, got["c0"], got["t_min"])
+    for key in ("t", "C", "parts_used", "max_n"):
+        assert got[key] == ref[key], (key, got[key], ref[key])
+    assert got["n"] == ref["n"]
+    assert got["first"] == ref["first"]
+    assert got["nsplit"] == ref["nsplit"]
+    if got["mode"] == "line":
+        assert got["start"] == ref["start"]
+    assert got["part_first_seq"] == ref["part_first_seq"]
+    assert max(got["nsplit"]) <= num_splits
+    assert got["clamped"] == 0
+    return got
+
+
+CASES = [
+    # (B, H, lens, S_max)
+    (3, 16, [1, 64, 300], 320),
+    (4, 128, [0, 65, 129, 1000], 1024),
+    (2, 32, [511, 37], 512),
+    (2, 144, [200, 77], 256),
+    (5, 128, [63, 64, 65, 128, 2], 128),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 32])
+def test_decode_small(case, num_splits):
+    B, H, lens, S = CASES[case]
+    say(f"decode B={B} H={H} lens={lens} S_max={S} num_splits={num_splits}")
+    d = workloads.decode_inputs(B, H, lens, S_max=S, seed=2000 + case)
+    o, l, ws = decode(d, num_splits)
+    check_plan(ws, d, num_splits)
+    Or, Lr = oracle_decode(d)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(l[b]))
+
+
+def test_decode_identical_rows_and_single_token():
+    H = 128
+    d = workloads.decode_inputs(3, H, [300, 1, 64], S_max=300, seed=2100)
+    d["cache"][0, :300] = d["cache"][0, 7]
+    o, l, _ = decode(d, 4)
+    ref_row = np64(d["cache"][0, 7, :512])
+    check_bf16(o[0], np.broadcast_to(ref_row, (H, 512)), "identical rows -> row")
+    assert torch.equal(o[1].cpu(), d["cache"][1, 0, :512].expand(H, -1))   # one token: P = 1 exactly
+    Or, Lr = oracle_decode(d)
+    check_lse(l, Lr, "LSE")
+
+
+def test_decode_fixed_length_workload_full():
+    d = workloads.mla_fixed_workload()
+    say("decode mla_fixed (B=16 H=128, 4096 tokens each) full compare")
+    o, l, ws = decode(d, 32)
+    check_plan(ws, d, 32)
+    Or, Lr = oracle_decode(d)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")
+
+
+@pytest.fixture(scope="module")
+def varlen():
+    return workloads.mla_varlen_workload()
+
+
+def test_decode_varlen_workload_sampled_and_deterministic(varlen):
+    d = varlen
+    say("absorb + decode mla_varlen (B=256 H=128, lengths 256..8192)")
+    ql = binding.mla_absorb_q(d["q_nope"].to(DEV), d["w_uk"].to(DEV))
+    qr, c, sl = d["q_rope"].to(DEV), d["cache"].to(DEV), d["seqlens"].to(DEV)
+    ws = binding.alloc_decode_workspace(256, 128, 32, DEV)
+    o1, l1 = binding.mla_decode_fwd(ql, qr, c, sl, SCALE, 32, workspace=ws)
+    o2, l2 = binding.mla_decode_fwd(ql, qr, c, sl, SCALE, 32, workspace=ws)
+    sync()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "run-to-run results differ"
+    dd = dict(seqlens=d["seqlens"], cache=d["cache"], q_lat=ql.cpu(), q_rope=d["q_rope"], q_nope=d["q_nope"])
+    check_plan(ws, dd, 32)
+    lens = d["seqlens"].tolist()
+    idx = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 128, 255})
+    say(f"  sampled sequences {idx} lengths {[lens[i] for i in idx]}")
+    # decode checked against the oracle on the kernel's own (bf16) q_lat ...
+    Or, Lr = oracle_decode(dd, idx)
+    check_bf16(o1[idx], Or, "O(sampled)")
+    check_lse(l1[idx], Lr, "LSE(sampled)")
+    # ... and end to end against explicit key decompression from q_nope.
+    i2 = idx[:3]
+    Lm = max(lens[i] for i in i2)
+    Oe, Le = OM.mla_decode_explicit_ref(np64(d["q_nope"][i2]), np64(d["q_rope"][i2]), np64(d["w_uk"]),
+                                        np64(d["cache"][i2, :Lm]), [lens[i] for i in i2], SCALE)
+    check_bf16(o1[i2], Oe, "O vs explicit decompression")
+    assert float(np.abs(np64(l1[i2]) - Le).max()) <= 2e-2
+
+
+def test_absorb_full_workload(varlen):
+    d = varlen
+    ql = binding.mla_absorb_q(d["q_nope"].to(DEV), d["w_uk"].to(DEV))
+    sync()
+    ref = OM.absorb_ref(np64(d["q_nope"]), np64(d["w_uk"]))
+    mx, rel = check_bf16(ql, ref, "q_lat")
+    assert rel <= 4e-3          # bf16 output rounding only (2^-9 relative)
+
+
+@pytest.mark.parametrize("B,H,Dn,Dl", [(1, 1, 32, 128), (5, 3, 64, 256), (70, 2, 128, 512), (3, 4, 512, 128)])
+def test_absorb_shapes(B, H, Dn, Dl):
+    g = torch.Generator().manual_seed(B * 1000 + Dn)
+    qn = torch.randn((B, H, Dn), generator=g).to(torch.bfloat16)
+    w = (torch.randn((H, Dn, Dl), generator=g) * 0.05).to(torch.bfloat16)
+    ql = binding.mla_absorb_q(qn.to(DEV), w.to(DEV))
+    sync()
+    ref = OM.absorb_ref(np64(qn), np64(w))
+    mx, rel = check_bf16(ql, ref, f"q_lat {B}x{H}x{Dn}x{Dl}")
+    assert rel <= 4e-3
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 32])
+def test_combine_standalone(S):
+    B, H = 3, 20
+    rng = np.random.default_rng(S)
+    o_part = rng.standard_normal((B, H, S, 512)).astype(np.float32)
+    lse_part = (rng.standard_normal((B, H, S)) * 3).astype(np.float32)
+    lse_part[rng.random((B, H, S)) < 0.3] = -np.inf
+    lse_part[0, 0, :] = -np.inf                    # a fully empty row
+    o, l = binding.mla_combine(torch.from_numpy(o_part).to(DEV), torch.from_numpy(lse_part).to(DEV))
+    sync()
+    Or, Lr = OM.combine_ref(o_part.astype(np.float64), lse_part.astype(np.float64))
+    check_bf16(o, Or, "combined O")
+    check_lse(l, Lr, "combined LSE")
+    assert torch.all(o[0, 0] == 0) and torch.isneginf(l[0, 0])
+
+
+def test_seqlens_out_of_range_are_clamped_and_flagged():
+    d = workloads.decode_inputs(2, 16, [100, 50], S_max=100, seed=2200)
+    d["seqlens"] = torch.tensor([150, -3], dtype=torch.int32)
+    o, l, ws = decode(d, 4)
+    got = binding.read_plan(ws, 2)
+    assert got["clamped"] == 2 and got["len"] == [100, 0]
+    d2 = dict(d, seqlens=torch.tensor([100, 0], dtype=torch.int32))
+    Or, Lr = oracle_decode(d2)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")
