@@ -19,7 +19,8 @@
 //                  rounded to bf16 with no data movement (see the key
 //                  permutation below).
 // Softmax runs in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e).
-// The accumulator is rescaled only when some row max of the wave grew.
+// The accumulator is rescaled only when some row max of the wave exceeds the
+// current exponent base by more than kRescaleSlack.
 // Masks follow section 3.4: tiles past the causal limit are never loaded;
 // the element mask is applied only on tiles that straddle the diagonal; keys
 // past N are clamped on load and masked.  A tile whose keys are all masked
@@ -159,17 +160,19 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
             for (int e = 1; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
             mt = max2_halves(mt) * c_log2;
-            const float m_new = fmaxf(m, mt);
-            const float mb = (m_new == -INFINITY) ? 0.f : m_new;
-            if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-                const float alpha = fast_exp2(m - mb);
+            // Lazy rescale (see kRescaleSlack): the base moves only when a
+            // row max exceeds it by more than the slack.
+            if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
+                const float m_new = fmaxf(m, mt);
+                const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
                 l *= alpha;
 #pragma unroll
                 for (int db = 0; db < B16_D / 32; ++db)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+                m = m_new;
             }
-            m = m_new;
+            const float mb = (m == -INFINITY) ? 0.f : m;
             bf16x8 pb[4];  // k-step ks (keys 16ks..16ks+15 of the tile)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {

@@ -26,6 +26,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Online softmax keeps an exponent base m (log2 domain) for each row and
+// forms p = exp2(s - m).  The base is raised -- and the accumulator and the
+// running sum rescaled by exp2(m_old - m_new) -- only when a row's new max
+// exceeds the base by more than this slack, so p <= 2^8.  Because l and the
+// accumulator always share the same base, O = acc / l and LSE = m + log2(l)
+// are unchanged; rescales become rare after the first tiles.
+constexpr float kRescaleSlack = 8.f;
+
 // ---------------------------------------------------------------------------
 // MFMA.  Operand layouts (verified on the device):
 //  16x16x32: A lane l holds row l%16, k = 8*(l/16)+[0..7];

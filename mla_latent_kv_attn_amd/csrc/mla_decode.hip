@@ -14,7 +14,7 @@
 //   1. mla_plan_kernel   (one workgroup): split plan from seqlens.
 //   2. mla_split_kernel  (one workgroup per part x 128-head block): streams
 //      the part's cache tiles through LDS and writes either the final output
-//      (sequence handled by one part) or an fp32 partial (o_s, lse_s).
+//      (sequence handled by one part) or a partial (o_s in bf16, lse_s fp32).
 //   3. mla_combine_slots_kernel: log-sum-exp merge of the partials of every
 //      split sequence; also writes o = 0, lse = -inf for empty sequences.
 //
@@ -25,7 +25,7 @@
 // (32 heads x 512 = 256 registers), which needs the full 512-entry register
 // file of a single wave per SIMD.  A 64-token tile (64 x 1152 B = 72 KiB) is
 // copied global -> LDS with global_load_lds_dwordx4 into one of two buffers
-// (147,456 B of LDS).  Per 32-token block and wave
+// (151,552 B of LDS).  Per 32-token block and wave
 // (v_mfma_f32_32x32x16_bf16):
 //   S^T = C q^T   A = cache rows from LDS (K = 576 = 36 steps), B = the
 //                 wave's q fragments.  Rows are fed in a permuted order so
@@ -46,28 +46,36 @@ constexpr int DEC_HEADS = 16;  // heads per wave
 constexpr int DEC_THREADS = DEC_WAVES * 64;
 static_assert(DEC_WAVES * DEC_HEADS == kDecodeHeadsPerWG, "head split");
 constexpr int DEC_ROW_CHUNKS = kRow * 2 / 16;                     // 72 chunks of 16 B per token
-constexpr int DEC_STRIDE_CHUNKS = DEC_ROW_CHUNKS + 1;             // +1 pad chunk per row in LDS
-constexpr int DEC_ROW_STRIDE = DEC_STRIDE_CHUNKS * 16;            // 1168 B (== 16 mod 128)
-constexpr int DEC_TILE_BYTES = kDecodeTile * DEC_ROW_STRIDE;      // 74752
-constexpr int DEC_TILE_INSTR = kDecodeTile * DEC_STRIDE_CHUNKS / 64;  // 73 wave-wide 1 KiB copies
-constexpr int DEC_SMEM = 2 * DEC_TILE_BYTES;                      // 149504
+constexpr int DEC_STRIDE_CHUNKS = DEC_ROW_CHUNKS + 2;             // +2 pad chunks per row in LDS
+constexpr int DEC_ROW_STRIDE = DEC_STRIDE_CHUNKS * 16;            // 1184 B (== 32 mod 128)
+constexpr int DEC_TILE_BYTES = kDecodeTile * DEC_ROW_STRIDE;      // 75776
+constexpr int DEC_TILE_INSTR = kDecodeTile * DEC_STRIDE_CHUNKS / 64;  // 74 wave-wide 1 KiB copies
+constexpr int DEC_SMEM = 2 * DEC_TILE_BYTES;                      // 151552
 static_assert(kDecodeTile * DEC_STRIDE_CHUNKS % 64 == 0, "whole copies");
 static_assert(DEC_SMEM <= 160 * 1024, "LDS");
-constexpr int DEC_LOADS_HI = (DEC_TILE_INSTR + DEC_WAVES - 1) / DEC_WAVES;  // copies issued by wave 0
-constexpr int DEC_LOADS_LO = DEC_TILE_INSTR / DEC_WAVES;                    // by the other waves
-static_assert(DEC_TILE_INSTR % DEC_WAVES == 1, "wave 0 issues the one extra copy");
-constexpr int DEC_PF = 2;  // LDS fragment prefetch distance, in MFMA steps
+constexpr int DEC_LOADS_HI = (DEC_TILE_INSTR + DEC_WAVES - 1) / DEC_WAVES;  // copies of waves < EXTRA
+constexpr int DEC_LOADS_LO = DEC_TILE_INSTR / DEC_WAVES;                    // copies of the other waves
+constexpr int DEC_LOADS_EXTRA = DEC_TILE_INSTR % DEC_WAVES;                 // waves issuing one more copy
+// LDS fragment prefetch distances, in MFMA steps, for the S^T and PV loops.
+#ifndef MLA_DEC_PF_QK
+#define MLA_DEC_PF_QK 2
+#endif
+#ifndef MLA_DEC_PF_PV
+#define MLA_DEC_PF_PV 6
+#endif
+constexpr int DEC_PF = MLA_DEC_PF_QK;
+constexpr int DEC_PFV = MLA_DEC_PF_PV;
 
 struct PlanArgs {
     int seq_len, seq_n, seq_start, seq_first, seq_nsplit, part_first_seq;  // int32 offsets
     long long o_part_off, lse_part_off;                                    // byte offsets
 };
 
-// LDS layout of a tile: token row r at byte r * 1168 (72 data chunks + 1
-// pad chunk).  With a row stride of 16 (mod 128) bytes, eight rows whose
-// indices differ in their low three bits fall on distinct 16-byte bank
-// groups, and four rows two apart (the transposed reads below) fall on
-// distinct 32-byte groups.
+// LDS layout of a tile: token row r at byte r * 1184 (72 data chunks + 2
+// pad chunks).  A row stride of 32 (mod 128) bytes is what measured free of
+// bank conflicts for the 16-row fragment reads of S^T (1152 runs 4x and
+// 1168 or 1216 2x slower on gfx950); the transposed reads run at the same
+// rate for every stride tried.
 
 // ---------------------------------------------------------------------------
 // 1. Plan.  Cost line: sequence b occupies n_b + c0 positions (n_b tiles
@@ -164,7 +172,7 @@ struct DecodeCtx {
     const __bf16* q_rope;
     const __bf16* cache;
     const int* ws;
-    float* o_part;
+    __bf16* o_part;
     float* lse_part;
     __bf16* o;
     float* lse;
@@ -173,10 +181,11 @@ struct DecodeCtx {
     PlanArgs a;
 };
 
-// Copy one 64-token tile to LDS: copy i (0..72) of 64 chunks is issued by
-// wave i % 4.  Chunk L of the tile is row L / 73, chunk L % 73 of that row;
-// the pad chunk (72) receives a second copy of chunk 0.  Rows past the
-// sequence end repeat its last token (finite data; their scores are masked).
+// Copy one 64-token tile to LDS: copy i (0..73) of 64 chunks is issued by
+// wave i % 8.  Chunk L of the tile is row L / 74, chunk L % 74 of that row;
+// the pad chunks (72, 73) receive second copies of chunks 0 and 1.  Rows past
+// the sequence end repeat its last token (finite data; their scores are
+// masked).
 __device__ __forceinline__ void dec_issue_tile(const DecodeCtx& x, char* buf, int b, int tok0, int len, int w,
                                                int lane) {
     const __bf16* seq = x.cache + (size_t)b * x.S_max * kRow;
@@ -184,14 +193,14 @@ __device__ __forceinline__ void dec_issue_tile(const DecodeCtx& x, char* buf, in
         const int L = i * 64 + lane;
         const int r = L / DEC_STRIDE_CHUNKS;
         int c = L - r * DEC_STRIDE_CHUNKS;
-        c = (c == DEC_ROW_CHUNKS) ? 0 : c;
+        c = (c >= DEC_ROW_CHUNKS) ? c - DEC_ROW_CHUNKS : c;
         const int tok = min(tok0 + r, len - 1);
         gload_lds16(seq + (size_t)tok * kRow + 8 * c, buf + i * 1024);
     }
 }
 
 __device__ __forceinline__ void dec_wait_prev_tile(int w) {
-    if (w == 0) wait_vmcnt<DEC_LOADS_HI>();
+    if (w < DEC_LOADS_EXTRA) wait_vmcnt<DEC_LOADS_HI>();
     else wait_vmcnt<DEC_LOADS_LO>();
 }
 
@@ -201,10 +210,8 @@ __device__ __forceinline__ void dec_wait_prev_tile(int w) {
 // second).  Lane group g of the results then holds, in its eight registers
 // (four per product), the tokens that the P^T operand of the PV product
 // assigns to logical k = 8g + e, and:
-//  * the 8 rows an 8-lane group reads for S^T have distinct low 3 bits
-//    (distinct 16-byte bank groups with the 1168-byte row stride);
-//  * the 4 rows a 16-lane ds_read_b64_tr_b16 touches are two apart
-//    (distinct 32-byte bank groups).
+//  * the rows an 8-lane group reads for S^T have distinct low 3 bits;
+//  * the 4 rows a 16-lane ds_read_b64_tr_b16 touches are two apart.
 __device__ __forceinline__ int dec_pi16(int i) { return 2 * (i & 3) + ((i >> 2) & 1) + 8 * (i >> 3); }
 __device__ __forceinline__ int dec_token_of(int g, int e) {  // e = 0..7 of lane group g
     return 16 * (e >> 2) + 2 * (e & 3) + (g & 1) + 8 * (g >> 1);
@@ -296,15 +303,19 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
                 float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
                                  fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
                 mt = max4_groups16(mt) * x.c_log2;
-                const float m_new = fmaxf(m, mt);
-                const float mb = (m_new == -INFINITY) ? 0.f : m_new;
-                if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-                    const float alpha = fast_exp2(m - mb);
+                // Lazy rescale: the exponent base m only moves when some
+                // head's max exceeds it by more than kRescaleSlack (P stays
+                // below 2^kRescaleSlack); l and the accumulator share the
+                // base, so the final O = acc / l is unchanged.
+                if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
+                    const float m_new = fmaxf(m, mt);
+                    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
                     l *= alpha;
 #pragma unroll
                     for (int db = 0; db < kLatent / 16; ++db) oacc[db] *= alpha;
+                    m = m_new;
                 }
-                m = m_new;
+                const float mb = (m == -INFINITY) ? 0.f : m;
                 bf16x8 pb;  // logical k = 8g + e
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -322,13 +333,13 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
                         return join(lds_read_tr16(pv_base, 32 * db),
                                     lds_read_tr16(pv_base, 16 * DEC_ROW_STRIDE + 32 * db));
                     };
-                    bf16x8 fv[DEC_PF + 1];
+                    bf16x8 fv[DEC_PFV + 1];
 #pragma unroll
-                    for (int i = 0; i < DEC_PF; ++i) fv[i] = rd(i);
+                    for (int i = 0; i < DEC_PFV; ++i) fv[i] = rd(i);
 #pragma unroll
                     for (int db = 0; db < NS; ++db) {
-                        if (db + DEC_PF < NS) fv[(db + DEC_PF) % (DEC_PF + 1)] = rd(db + DEC_PF);
-                        oacc[db] = mfma16(fv[db % (DEC_PF + 1)], pb, oacc[db]);
+                        if (db + DEC_PFV < NS) fv[(db + DEC_PFV) % (DEC_PFV + 1)] = rd(db + DEC_PFV);
+                        oacc[db] = mfma16(fv[db % (DEC_PFV + 1)], pb, oacc[db]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -354,10 +365,18 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
         }
         if (x.lse && g == 0) x.lse[(size_t)b * H + head] = lse_v;
     } else {
+        // Partial of a split sequence: normalised over this piece, stored in
+        // bf16 (the merge weights sum to one, so its rounding stays at the
+        // level of the final bf16 output's).
         const int slot = 2 * p + (x.ws[x.a.part_first_seq + p] == b ? 0 : 1);
-        float* op = x.o_part + ((size_t)slot * H + head) * kLatent + 4 * g;
+        __bf16* op = x.o_part + ((size_t)slot * H + head) * kLatent + 4 * g;
 #pragma unroll
-        for (int db = 0; db < kLatent / 16; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = oacc[db] * inv_l;
+        for (int db = 0; db < kLatent / 16; ++db) {
+            bf16x4 t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][r] * inv_l);
+            *reinterpret_cast<bf16x4*>(op + 16 * db) = t;
+        }
         if (g == 0) x.lse_part[(size_t)slot * H + head] = lse_v;
     }
 }
@@ -388,68 +407,94 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) 
 // ---------------------------------------------------------------------------
 // 3. Combine: lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.
 //    Empty splits (lse_s = -inf) weigh 0; all empty -> o = 0, lse = -inf.
+//    A workgroup of 256 threads serves 4 heads of one sequence; a thread owns
+//    8 consecutive output dims.  The per-split loads are independent, so
+//    they are issued back to back.
 // ---------------------------------------------------------------------------
-template <typename SlotFn>
-__device__ __forceinline__ void combine_row(const float* o_part, const float* lse_part, size_t row_stride_o,
-                                            int nsplit, SlotFn slot_of, __bf16* o_row, float* lse_out, int d4) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse_part[slot_of(s)]);
-    if (M == -INFINITY) {
-        *reinterpret_cast<bf16x4*>(o_row + 4 * d4) = bf16x4{to_bf16(0.f), to_bf16(0.f), to_bf16(0.f), to_bf16(0.f)};
-        if (lse_out && d4 == 0) *lse_out = -INFINITY;
-        return;
-    }
-    float W = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-        const size_t sl = slot_of(s);
-        const float ls = lse_part[sl];
-        const float wgt = (ls == -INFINITY) ? 0.f : __expf(ls - M);
-        W += wgt;
-        if (wgt != 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(o_part + sl * row_stride_o + 4 * d4);
-    }
-    const float inv = 1.f / W;
-    bf16x4 t;
+constexpr int CMB_THREADS = 256;
+constexpr int CMB_HEADS = CMB_THREADS / (kLatent / 8);  // 4
+
+__device__ __forceinline__ void load8(const __bf16* p, float* v) {
+    const bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[r] * inv);
-    *reinterpret_cast<bf16x4*>(o_row + 4 * d4) = t;
-    if (lse_out && d4 == 0) *lse_out = M + __logf(W);
+    for (int i = 0; i < 8; ++i) v[i] = (float)t[i];
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
 }
 
-// Partials of the split kernel: slot-major [slots][H][512].
-__global__ __launch_bounds__(256) void mla_combine_slots_kernel(const int* __restrict__ ws, const float* o_part,
-                                                               const float* lse_part, __bf16* o, float* lse,
-                                                               int H, PlanArgs a) {
+// rows(s) gives the row index of split s in lse_part (and, times 512, in o_part).
+template <typename PT, typename RowFn>
+__device__ __forceinline__ void combine_head(const PT* o_part, const float* lse_part, int nsplit, RowFn rows,
+                                             __bf16* o_row, float* lse_out, int d8) {
+    float M = -INFINITY;
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse_part[rows(s)]);
+    bf16x8 out;
+    if (M == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = to_bf16(0.f);
+        *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = out;
+        if (lse_out && d8 == 0) *lse_out = -INFINITY;
+        return;
+    }
+    float W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) {
+        const size_t r = rows(s);
+        const float ls = lse_part[r];
+        const float wgt = (ls == -INFINITY) ? 0.f : __expf(ls - M);
+        float v[8];
+        load8(o_part + r * kLatent + 8 * d8, v);
+        W += wgt;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = (wgt == 0.f) ? acc[i] : __builtin_fmaf(wgt, v[i], acc[i]);
+    }
+    const float inv = 1.f / W;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = to_bf16(acc[i] * inv);
+    *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = out;
+    if (lse_out && d8 == 0) *lse_out = M + __logf(W);
+}
+
+// Partials of the split kernel: slot-major [slots][H][512] bf16, lse [slots][H].
+__global__ __launch_bounds__(CMB_THREADS) void mla_combine_slots_kernel(const int* __restrict__ ws,
+                                                                       const __bf16* __restrict__ o_part,
+                                                                       const float* __restrict__ lse_part,
+                                                                       __bf16* __restrict__ o, float* lse, int H,
+                                                                       PlanArgs a) {
     const int b = blockIdx.x;
     const int ns = ws[a.seq_nsplit + b];
     if (ns == 1) return;
+    const int hh = blockIdx.y * CMB_HEADS + (threadIdx.x >> 6);
+    if (hh >= H) return;
+    const int d8 = threadIdx.x & 63;
     const int first = ws[a.seq_first + b];
-    const int d4 = threadIdx.x & 127;
     const int* pfs = ws + a.part_first_seq;
-    for (int hh = blockIdx.y * 16 + (threadIdx.x >> 7); hh < min(H, (int)(blockIdx.y + 1) * 16); hh += 2) {
-        __bf16* orow = o + ((size_t)b * H + hh) * kLatent;
-        float* lrow = lse ? lse + (size_t)b * H + hh : nullptr;
-        auto slot_of = [&](int s) -> size_t {
-            const int p = first + s;
-            const int slot = 2 * p + (pfs[p] == b ? 0 : 1);
-            return (size_t)slot * H + hh;
-        };
-        // row index = slot*H + hh, so o_part row stride is kLatent floats
-        combine_row(o_part, lse_part, kLatent, ns, slot_of, orow, lrow, d4);
-    }
+    auto rows = [&](int s) -> size_t {
+        const int p = first + s;
+        return (size_t)(2 * p + (pfs[p] == b ? 0 : 1)) * H + hh;
+    };
+    combine_head(o_part, lse_part, ns, rows, o + ((size_t)b * H + hh) * kLatent,
+                 lse ? lse + (size_t)b * H + hh : nullptr, d8);
 }
 
-// Caller-supplied dense partials: o_part [B,H,S,512], lse_part [B,H,S].
-__global__ __launch_bounds__(256) void mla_combine_dense_kernel(const float* o_part, const float* lse_part,
-                                                               __bf16* o, float* lse, int H, int S) {
+// Caller-supplied dense partials: o_part [B,H,S,512] fp32, lse_part [B,H,S].
+__global__ __launch_bounds__(CMB_THREADS) void mla_combine_dense_kernel(const float* __restrict__ o_part,
+                                                                       const float* __restrict__ lse_part,
+                                                                       __bf16* __restrict__ o, float* lse, int H,
+                                                                       int S) {
     const int b = blockIdx.x;
-    const int d4 = threadIdx.x & 127;
-    for (int hh = blockIdx.y * 16 + (threadIdx.x >> 7); hh < min(H, (int)(blockIdx.y + 1) * 16); hh += 2) {
-        const size_t row0 = ((size_t)b * H + hh) * S;
-        auto slot_of = [&](int s) -> size_t { return row0 + s; };
-        combine_row(o_part, lse_part, kLatent, S, slot_of, o + ((size_t)b * H + hh) * kLatent,
-                    lse ? lse + (size_t)b * H + hh : nullptr, d4);
-    }
+    const int hh = blockIdx.y * CMB_HEADS + (threadIdx.x >> 6);
+    if (hh >= H) return;
+    const int d8 = threadIdx.x & 63;
+    const size_t row0 = ((size_t)b * H + hh) * S;
+    auto rows = [&](int s) -> size_t { return row0 + s; };
+    combine_head(o_part, lse_part, S, rows, o + ((size_t)b * H + hh) * kLatent,
+                 lse ? lse + (size_t)b * H + hh : nullptr, d8);
 }
 
 // ---------------------------------------------------------------------------
@@ -494,7 +539,7 @@ hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __
     x.q_rope = q_rope;
     x.cache = cache;
     x.ws = ws;
-    x.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_part_bytes_off);
+    x.o_part = reinterpret_cast<__bf16*>(static_cast<char*>(workspace) + L.o_part_bytes_off);
     x.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_part_bytes_off);
     x.o = o;
     x.lse = lse;
@@ -504,15 +549,15 @@ hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __
     x.a = a;
     const int hblocks = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
     hipLaunchKernelGGL(mla_split_kernel, dim3(L.parts, hblocks), dim3(DEC_THREADS), DEC_SMEM, stream, x);
-    hipLaunchKernelGGL(mla_combine_slots_kernel, dim3(B, (H + 15) / 16), dim3(256), 0, stream, ws, x.o_part,
-                       x.lse_part, o, lse, H, a);
+    hipLaunchKernelGGL(mla_combine_slots_kernel, dim3(B, (H + CMB_HEADS - 1) / CMB_HEADS), dim3(CMB_THREADS), 0,
+                       stream, ws, x.o_part, x.lse_part, o, lse, H, a);
     return hipGetLastError();
 }
 
 hipError_t launch_mla_combine(const float* o_part, const float* lse_part, __bf16* o, float* lse, int B, int H,
                               int S, hipStream_t stream) {
-    hipLaunchKernelGGL(mla_combine_dense_kernel, dim3(B, (H + 15) / 16), dim3(256), 0, stream, o_part, lse_part, o,
-                       lse, H, S);
+    hipLaunchKernelGGL(mla_combine_dense_kernel, dim3(B, (H + CMB_HEADS - 1) / CMB_HEADS), dim3(CMB_THREADS), 0,
+                       stream, o_part, lse_part, o, lse, H, S);
     return hipGetLastError();
 }
 

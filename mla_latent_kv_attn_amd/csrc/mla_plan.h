@@ -39,7 +39,7 @@ enum PlanWord {
 struct PlanLayout {
     // int32 offsets (in elements) of each array from the workspace start
     size_t seq_len, seq_n, seq_start, seq_first, seq_nsplit, part_first_seq;
-    // byte offsets of the fp32 partial results
+    // byte offsets of the partial results (bf16 outputs, fp32 LSE)
     size_t o_part_bytes_off, lse_part_bytes_off;
     size_t total_bytes;
     int parts;      // grid size of the split kernel
@@ -61,7 +61,7 @@ inline PlanLayout plan_layout(int B, int H, int parts, int slots) {
     L.part_first_seq = off; off += (size_t)parts;
     size_t bytes = align_up(off * 4, 256);
     L.o_part_bytes_off = bytes;
-    bytes += (size_t)slots * H * kLatent * 4;
+    bytes += (size_t)slots * H * kLatent * 2;  // bf16 partial outputs
     bytes = align_up(bytes, 256);
     L.lse_part_bytes_off = bytes;
     bytes += (size_t)slots * H * 4;

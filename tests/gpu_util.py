@@ -56,7 +56,8 @@ def check_lse(l_gpu, l_ref, what):
     lg, lr = np64(l_gpu), np.asarray(l_ref, dtype=np.float64)
     both_inf = np.isneginf(lg) & np.isneginf(lr)
     assert np.array_equal(np.isneginf(lg), np.isneginf(lr)), f"{what}: -inf pattern differs"
-    d = np.abs(np.where(both_inf, 0.0, lg - lr))
+    with np.errstate(invalid="ignore"):
+        d = np.abs(np.where(both_inf, 0.0, lg - lr))
     mx = float(d.max()) if d.size else 0.0
     say(f"  {what}: max|dLSE|={mx:.3e}")
     assert mx <= TOL_LSE, f"{what}: LSE max abs {mx}"
