@@ -41,8 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
-    ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32"], default=None,
-                    help="run only one workload (for profiling)")
+    ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32", "copy"], default=None,
+                    help="run only one workload (for profiling); 'copy' is a plain 256 MiB device copy "
+                         "used to calibrate the HBM byte counters")
     return ap.parse_args()
 
 
@@ -142,6 +143,45 @@ def bench_prefill(log, name, causal, reps=10):
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
 
 
+DECODE_SOURCES = ("mla_latent_kv_attn_amd/csrc/mla_decode.hip", "mla_latent_kv_attn_amd/csrc/mla_plan.h",
+                  "mla_latent_kv_attn_amd/csrc/common.h")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_varlen_pmc.json")
+
+
+def decode_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(log):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it was taken on different kernel sources than the ones built here."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != decode_sources_sha():
+        log("traffic: counter summary is stale (kernel sources changed); reporting null")
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def plain_copy():
+    import torch
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes 3 times", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(d, log, budget_s=12.0):
     """Time the oracle (as it stands) on a bounded sample of the decode workload."""
     import numpy as np
@@ -186,6 +226,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.only == "copy":
+        plain_copy()
+        return
     if args.only == "prefill_bf16":
         bench_prefill(log, "attn_bf16", True, reps=args.steps)
         return
@@ -223,7 +266,7 @@ def main():
                    "kv_bytes_per_step": d["kv_bytes"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "mla_decode_fwd (plan + split + combine kernels)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(log),
                      "decode_us": round(d["dec_ms"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "prefill": prefill,
