@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -83,6 +85,20 @@ __device__ __forceinline__ void gload_lds16(const void* gsrc, void* lds_wave_bas
                                      (void MLA_LDS*)lds_wave_base, 16, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, so the record
+// count is a byte count; the fourth descriptor word selects 32-bit data
+// format as gfx9 raw buffers require).  Buffer reads at or past `bytes`
+// return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer -> LDS copy of 16 bytes per lane from byte offset `voff` of the
+// buffer; like gload_lds16, the wave's chunks land at lds_wave_base + 16*lane.
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)lds_wave_base, 16, (int)voff, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 template <int N>
@@ -92,6 +108,53 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// ---------------------------------------------------------------------------
+// Explicitly scheduled LDS fragment reads.
+//
+// The compiler treats every LDS read as possibly aliasing in-flight
+// direct-to-LDS copies and waits for all of them (vmcnt(0)), and it also
+// drains every outstanding LDS read (lgkmcnt(0)) before each use.  In the
+// tile loops that would serialise the multi-tile copy pipeline and the
+// fragment prefetch.  The loops therefore issue their fragment reads with
+// these asm forms, which the compiler does not count, and wait for them with
+// wait_lgkm<N>() where N is the exact number of reads issued after the one
+// being consumed (the issue order is pinned with sched_barrier).  Only LDS
+// reads count in lgkmcnt inside those loops: the copies count in vmcnt and
+// the loops issue no scalar memory reads.
+// ---------------------------------------------------------------------------
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((const MLA_LDS char*)(p));
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 ds_read16(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    bf16x8 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x4 ds_read_tr16(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (N << 8) | (3 << 14));
 }
 
 // ---------------------------------------------------------------------------

@@ -18,19 +18,19 @@
 //   3. mla_combine_slots_kernel: log-sum-exp merge of the partials of every
 //      split sequence; also writes o = 0, lse = -inf for empty sequences.
 //
-// Split-kernel tiling.  A workgroup has 4 waves (one per SIMD); wave w owns
-// 32 heads, so the workgroup serves 128 heads and every cache byte crosses
-// HBM -> LDS once for all of them.  Per wave the state is the q fragments
-// (32 heads x 576 bf16 = 144 VGPRs) and the fp32 output accumulator
-// (32 heads x 512 = 256 registers), which needs the full 512-entry register
-// file of a single wave per SIMD.  A 64-token tile (64 x 1152 B = 72 KiB) is
-// copied global -> LDS with global_load_lds_dwordx4 into one of two buffers
-// (151,552 B of LDS).  Per 32-token block and wave
-// (v_mfma_f32_32x32x16_bf16):
-//   S^T = C q^T   A = cache rows from LDS (K = 576 = 36 steps), B = the
-//                 wave's q fragments.  Rows are fed in a permuted order so
-//                 that lane (head, g) ends with tokens 16ks+8g..+7 of each
-//                 16-token k-step in consecutive registers.
+// Split-kernel design.  A workgroup has 8 waves (two per SIMD); wave w owns
+// 16 heads, so one workgroup serves 128 heads and every cache byte crosses
+// HBM -> LDS once for all of them.  Per wave the q fragments (16 heads x
+// 576 bf16 = 72 VGPRs) and the fp32 output accumulator (16 x 512 = 128
+// VGPRs) stay in registers.  The cache streams through a ring of four
+// 32-token LDS tiles (4 x 37,888 B) filled by global_load_lds_dwordx4, so
+// three tiles (~111 KiB per CU) are in flight while one is computed: with a
+// single tile in flight the kernel is bound by memory latency, not by
+// bandwidth.  Per tile and wave (v_mfma_f32_16x16x32_bf16):
+//   S^T = C q^T   A = cache rows from LDS (K = 576 = 18 steps, two products
+//                 of 16 tokens), B = the wave's q fragments.  Tokens are fed
+//                 in a permuted order so that the S^T registers already form
+//                 the P^T operand of the PV product.
 //   O^T += C^T P^T  A = latent columns read transposed with
 //                 ds_read_b64_tr_b16 from the same LDS tile, B = P in bf16.
 // The same LDS bytes serve as key (576 dims) and value (first 512 dims).
@@ -48,23 +48,31 @@ static_assert(DEC_WAVES * DEC_HEADS == kDecodeHeadsPerWG, "head split");
 constexpr int DEC_ROW_CHUNKS = kRow * 2 / 16;                     // 72 chunks of 16 B per token
 constexpr int DEC_STRIDE_CHUNKS = DEC_ROW_CHUNKS + 2;             // +2 pad chunks per row in LDS
 constexpr int DEC_ROW_STRIDE = DEC_STRIDE_CHUNKS * 16;            // 1184 B (== 32 mod 128)
-constexpr int DEC_TILE_BYTES = kDecodeTile * DEC_ROW_STRIDE;      // 75776
-constexpr int DEC_TILE_INSTR = kDecodeTile * DEC_STRIDE_CHUNKS / 64;  // 74 wave-wide 1 KiB copies
-constexpr int DEC_SMEM = 2 * DEC_TILE_BYTES;                      // 151552
-static_assert(kDecodeTile * DEC_STRIDE_CHUNKS % 64 == 0, "whole copies");
+constexpr int DEC_TILE = 32;                                      // tokens per LDS tile (one MFMA k-step of PV)
+constexpr int DEC_NBUF = 4;                                       // tiles in the LDS ring
+constexpr int DEC_AHEAD = DEC_NBUF - 2;                           // tiles in flight (one tile is computed, one
+                                                                  // kept for the lagging wave group's PV)
+constexpr int DEC_TILE_BYTES = DEC_TILE * DEC_ROW_STRIDE;         // 37888
+constexpr int DEC_TILE_INSTR = DEC_TILE * DEC_STRIDE_CHUNKS / 64; // 37 wave-wide 1 KiB copies per tile
+constexpr int DEC_SMEM = DEC_NBUF * DEC_TILE_BYTES;               // 151552
+static_assert(DEC_TILE * DEC_STRIDE_CHUNKS % 64 == 0, "whole copies");
 static_assert(DEC_SMEM <= 160 * 1024, "LDS");
+static_assert(kDecodeTile % DEC_TILE == 0, "plan tiles are whole LDS tiles");
 constexpr int DEC_LOADS_HI = (DEC_TILE_INSTR + DEC_WAVES - 1) / DEC_WAVES;  // copies of waves < EXTRA
 constexpr int DEC_LOADS_LO = DEC_TILE_INSTR / DEC_WAVES;                    // copies of the other waves
 constexpr int DEC_LOADS_EXTRA = DEC_TILE_INSTR % DEC_WAVES;                 // waves issuing one more copy
+
 // LDS fragment prefetch distances, in MFMA steps, for the S^T and PV loops.
 #ifndef MLA_DEC_PF_QK
 #define MLA_DEC_PF_QK 2
 #endif
 #ifndef MLA_DEC_PF_PV
-#define MLA_DEC_PF_PV 6
+#define MLA_DEC_PF_PV 4
 #endif
 constexpr int DEC_PF = MLA_DEC_PF_QK;
 constexpr int DEC_PFV = MLA_DEC_PF_PV;
+static_assert(DEC_PF <= DEC_PFV, "PV ring slots 0..DEC_PF-1 are filled during the S^T tail");
+static_assert(2 * DEC_PF < 16 && 2 * DEC_PFV < 16, "lgkmcnt range");
 
 struct PlanArgs {
     int seq_len, seq_n, seq_start, seq_first, seq_nsplit, part_first_seq;  // int32 offsets
@@ -181,27 +189,39 @@ struct DecodeCtx {
     PlanArgs a;
 };
 
-// Copy one 64-token tile to LDS: copy i (0..73) of 64 chunks is issued by
+// Copy one 32-token tile to LDS: copy i (0..36) of 64 chunks is issued by
 // wave i % 8.  Chunk L of the tile is row L / 74, chunk L % 74 of that row;
-// the pad chunks (72, 73) receive second copies of chunks 0 and 1.  Rows past
-// the sequence end repeat its last token (finite data; their scores are
-// masked).
-__device__ __forceinline__ void dec_issue_tile(const DecodeCtx& x, char* buf, int b, int tok0, int len, int w,
-                                               int lane) {
-    const __bf16* seq = x.cache + (size_t)b * x.S_max * kRow;
-    for (int i = w; i < DEC_TILE_INSTR; i += DEC_WAVES) {
-        const int L = i * 64 + lane;
+// the pad chunks (72, 73) receive second copies of chunks 0 and 1.  Each
+// wave's per-lane source offsets within a tile are fixed (dec_copy_offsets);
+// a tile only moves the buffer resource, whose size ends at the sequence's
+// last token, so rows past the end read as zeros (their scores are masked).
+__device__ __forceinline__ void dec_copy_offsets(uint32_t (&voff)[DEC_LOADS_HI], int w, int lane) {
+#pragma unroll
+    for (int k = 0; k < DEC_LOADS_HI; ++k) {
+        const int L = (w + DEC_WAVES * k) * 64 + lane;
         const int r = L / DEC_STRIDE_CHUNKS;
         int c = L - r * DEC_STRIDE_CHUNKS;
         c = (c >= DEC_ROW_CHUNKS) ? c - DEC_ROW_CHUNKS : c;
-        const int tok = min(tok0 + r, len - 1);
-        gload_lds16(seq + (size_t)tok * kRow + 8 * c, buf + i * 1024);
+        voff[k] = (uint32_t)(r * kRow * 2 + 16 * c);
     }
 }
 
-__device__ __forceinline__ void dec_wait_prev_tile(int w) {
-    if (w < DEC_LOADS_EXTRA) wait_vmcnt<DEC_LOADS_HI>();
-    else wait_vmcnt<DEC_LOADS_LO>();
+__device__ __forceinline__ void dec_issue_tile(const __bf16* seq, int len, int tok0, char* buf,
+                                               const uint32_t (&voff)[DEC_LOADS_HI], int w) {
+    const auto rsrc = make_rsrc(seq + (size_t)tok0 * kRow, (uint32_t)(len - tok0) * (uint32_t)(kRow * 2));
+    static_for<DEC_LOADS_HI>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        if (k < DEC_LOADS_LO || w < DEC_LOADS_EXTRA)
+            bload_lds16(rsrc, buf + (w + DEC_WAVES * k) * 1024, voff[k]);
+    });
+}
+
+// Wait until this wave's copies of the oldest in-flight tile have landed,
+// leaving `later` younger tiles in flight.
+template <int LATER>
+__device__ __forceinline__ void dec_wait_tile(int w) {
+    if (w < DEC_LOADS_EXTRA) wait_vmcnt<LATER * DEC_LOADS_HI>();
+    else wait_vmcnt<LATER * DEC_LOADS_LO>();
 }
 
 // Token permutation inside a 32-token block, for v_mfma_f32_16x16x32_bf16.
@@ -217,7 +237,8 @@ __device__ __forceinline__ int dec_token_of(int g, int e) {  // e = 0..7 of lane
     return 16 * (e >> 2) + 2 * (e & 3) + (g & 1) + 8 * (g >> 1);
 }
 
-__device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile_lo, int tile_hi) {
+__device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile_lo, int tile_hi, int len,
+                          int nsplit, bool first_in_part) {
     const int w = wave_id();
     const int lane = lane_id();
     const int n = lane & 15;  // head column of the MFMA results / MFMA row of the A operand
@@ -226,19 +247,7 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     const int hbase = blockIdx.y * kDecodeHeadsPerWG + DEC_HEADS * w;
     const bool active = hbase < H;  // H % 16 == 0: a wave is fully in or out
     const int head = hbase + n;
-    const int len = x.ws[x.a.seq_len + b];
     const int tok_end = min(tile_hi * kDecodeTile, len);
-
-    // q as the B operand of S^T = C q^T: lane (head n, g) holds dims 32kk+8g..+7.
-    bf16x8 qf[kRow / 32];
-    if (active) {
-        const bf16x8* ql = reinterpret_cast<const bf16x8*>(x.q_lat + ((size_t)b * H + head) * kLatent);
-        const bf16x8* qr = reinterpret_cast<const bf16x8*>(x.q_rope + ((size_t)b * H + head) * kRope);
-#pragma unroll
-        for (int kk = 0; kk < kLatent / 32; ++kk) qf[kk] = ql[4 * kk + g];
-#pragma unroll
-        for (int kk = 0; kk < kRope / 32; ++kk) qf[kLatent / 32 + kk] = qr[4 * kk + g];
-    }
 
     f32x4 oacc[kLatent / 16];
 #pragma unroll
@@ -249,112 +258,152 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     const int qk_off = dec_pi16(n) * DEC_ROW_STRIDE + 16 * g;
     const int jj = n >> 2, qd = n & 3;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
     const int pv_off = dec_pi16(4 * g + jj) * DEC_ROW_STRIDE + 8 * qd;
-    const int ntiles = tile_hi - tile_lo;
+    // The piece covers plan tiles [tile_lo, tile_hi); LDS tiles are 32 tokens.
+    const int tok_lo = tile_lo * kDecodeTile;
+    const int ntiles = (tok_end - tok_lo + DEC_TILE - 1) / DEC_TILE;
 
-    dec_issue_tile(x, smem, b, tile_lo * kDecodeTile, len, w, lane);
-    for (int j = 0; j < ntiles; ++j) {
-        char* cur = smem + (j & 1) * DEC_TILE_BYTES;
-        if (j + 1 < ntiles) {
-            dec_issue_tile(x, smem + ((j + 1) & 1) * DEC_TILE_BYTES, b, (tile_lo + j + 1) * kDecodeTile, len, w,
-                           lane);
-            dec_wait_prev_tile(w);
-        } else {
-            wait_vmcnt<0>();
-        }
-        lds_barrier();
-        if (active) {
-            const int valid = tok_end - (tile_lo + j) * kDecodeTile;  // >= 1
+    // Ring of DEC_NBUF LDS tiles.  DEC_AHEAD tiles are in flight while tile j
+    // is computed, enough outstanding HBM reads per CU to cover the memory
+    // latency.  The two waves sharing a SIMD run half a tile apart: group A
+    // (waves 0-3) does S^T, softmax and PV of tile j; group B (waves 4-7)
+    // first finishes PV of tile j-1, then S^T and softmax of tile j, so one
+    // wave's softmax overlaps the other's matrix work.  One barrier per tile
+    // publishes tile j (every wave has waited for its own copies) and proves
+    // tile j-2 fully consumed, so tile j+DEC_AHEAD can be copied into its
+    // buffer right after it.
+    const bool lag = w >= DEC_WAVES / 2;
+    const __bf16* seq = x.cache + (size_t)b * x.S_max * kRow;
+    uint32_t voff[DEC_LOADS_HI];
+    dec_copy_offsets(voff, w, lane);
 #pragma unroll
-            for (int tb = 0; tb < kDecodeTile / 32; ++tb) {
-                // ---- scores for tokens 32tb..32tb+31: sa (first 16), sb (second 16) ----
-                const char* qk_base = cur + qk_off + 32 * tb * DEC_ROW_STRIDE;
-                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-                {
-                    // Fragment reads run DEC_PF steps ahead of the MFMAs that
-                    // consume them; schedule barriers keep the compiler from
-                    // hoisting every read (which would exhaust the VGPRs).
-                    constexpr int KS = kRow / 32;
-                    bf16x8 fa[DEC_PF + 1], fb[DEC_PF + 1];
+    for (int i = 0; i < DEC_AHEAD; ++i)
+        if (i < ntiles) dec_issue_tile(seq, len, tok_lo + i * DEC_TILE, smem + i * DEC_TILE_BYTES, voff, w);
+
+    // q fragments (loaded after the first tile copies are in flight) as the B
+    // operand of S^T = C q^T: lane (head n, g) holds dims 32kk+8g..+7.
+    bf16x8 qf[kRow / 32];
+    if (active) {
+        const bf16x8* ql = reinterpret_cast<const bf16x8*>(x.q_lat + ((size_t)b * H + head) * kLatent);
+        const bf16x8* qr = reinterpret_cast<const bf16x8*>(x.q_rope + ((size_t)b * H + head) * kRope);
 #pragma unroll
-                    for (int i = 0; i < DEC_PF; ++i) {
-                        fa[i] = lds_read16(qk_base, 64 * i);
-                        fb[i] = lds_read16(qk_base, 16 * DEC_ROW_STRIDE + 64 * i);
-                    }
+        for (int kk = 0; kk < kLatent / 32; ++kk) qf[kk] = ql[4 * kk + g];
 #pragma unroll
-                    for (int kk = 0; kk < KS; ++kk) {
-                        if (kk + DEC_PF < KS) {
-                            fa[(kk + DEC_PF) % (DEC_PF + 1)] = lds_read16(qk_base, 64 * (kk + DEC_PF));
-                            fb[(kk + DEC_PF) % (DEC_PF + 1)] =
-                                lds_read16(qk_base, 16 * DEC_ROW_STRIDE + 64 * (kk + DEC_PF));
-                        }
-                        sa = mfma16(fa[kk % (DEC_PF + 1)], qf[kk], sa);
-                        sb = mfma16(fb[kk % (DEC_PF + 1)], qf[kk], sb);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                if (valid < 32 * tb + 32) {
+        for (int kk = 0; kk < kRope / 32; ++kk) qf[kLatent / 32 + kk] = qr[4 * kk + g];
+    }
+
+
+    constexpr int KS = kRow / 32;      // S^T k-steps
+    constexpr int NS = kLatent / 16;   // PV dim blocks
+    bf16x8 fa[DEC_PF + 1], fb[DEC_PF + 1], fv[DEC_PFV + 1];
+    bf16x8 pb_prev;                    // P of tile j-1 (lagging group)
+    uint32_t pv_prev = 0;              // LDS address of tile j-1's PV fragments
+
+    // Fragment rings: S^T fragments (fa, fb) run DEC_PF steps ahead of the
+    // MFMAs that consume them, PV fragments (fv) DEC_PFV steps.  Every S^T
+    // step issues one unit of two reads, so when step kk's pair is consumed
+    // exactly 2*DEC_PF newer reads are outstanding; PV step db has
+    // 2*min(DEC_PFV, NS-1-db).  Schedule barriers pin this order.
+    auto pv_phase = [&](uint32_t pv_a, const bf16x8& p) {
+        auto rd_pv = [&](auto db_c) {
+            constexpr int db = decltype(db_c)::value;
+            fv[db % (DEC_PFV + 1)] = join(ds_read_tr16<32 * db>(pv_a),
+                                          ds_read_tr16<16 * DEC_ROW_STRIDE + 32 * db>(pv_a));
+        };
+        static_for<DEC_PFV>([&](auto i) { rd_pv(i); });
+        static_for<NS>([&](auto db_c) {
+            constexpr int db = decltype(db_c)::value;
+            if constexpr (db + DEC_PFV < NS) rd_pv(std::integral_constant<int, db + DEC_PFV>{});
+            constexpr int newer = 2 * ((NS - 1 - db) < DEC_PFV ? (NS - 1 - db) : DEC_PFV);
+            wait_lgkm<newer>();
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[db] = mfma16(fv[db % (DEC_PFV + 1)], p, oacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // S^T for the tile's 32 tokens (sa: first 16, sb: second 16), masks,
+    // online softmax (log2 domain) and P in bf16.
+    auto qk_softmax = [&](uint32_t qk_a, int valid) -> bf16x8 {
+        auto rd_qk = [&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            fa[kk % (DEC_PF + 1)] = ds_read16<64 * kk>(qk_a);
+            fb[kk % (DEC_PF + 1)] = ds_read16<16 * DEC_ROW_STRIDE + 64 * kk>(qk_a);
+        };
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+        static_for<DEC_PF>([&](auto i) { rd_qk(i); });
+        static_for<KS>([&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            if constexpr (kk + DEC_PF < KS) rd_qk(std::integral_constant<int, kk + DEC_PF>{});
+            constexpr int newer = 2 * ((KS - 1 - kk) < DEC_PF ? (KS - 1 - kk) : DEC_PF);
+            wait_lgkm<newer>();
+            __builtin_amdgcn_sched_barrier(0);
+            sa = mfma16(fa[kk % (DEC_PF + 1)], qf[kk], sa);
+            sb = mfma16(fb[kk % (DEC_PF + 1)], qf[kk], sb);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (valid < DEC_TILE) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (32 * tb + dec_token_of(g, r) >= valid) sa[r] = -INFINITY;
-                        if (32 * tb + dec_token_of(g, 4 + r) >= valid) sb[r] = -INFINITY;
-                    }
-                }
-                // ---- online softmax (log2 domain) ----
-                float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
-                                 fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-                mt = max4_groups16(mt) * x.c_log2;
-                // Lazy rescale: the exponent base m only moves when some
-                // head's max exceeds it by more than kRescaleSlack (P stays
-                // below 2^kRescaleSlack); l and the accumulator share the
-                // base, so the final O = acc / l is unchanged.
-                if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
-                    const float m_new = fmaxf(m, mt);
-                    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
-                    l *= alpha;
-#pragma unroll
-                    for (int db = 0; db < kLatent / 16; ++db) oacc[db] *= alpha;
-                    m = m_new;
-                }
-                const float mb = (m == -INFINITY) ? 0.f : m;
-                bf16x8 pb;  // logical k = 8g + e
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float pa = fast_exp2(__builtin_fmaf(sa[r], x.c_log2, -mb));
-                    const float pq = fast_exp2(__builtin_fmaf(sb[r], x.c_log2, -mb));
-                    l += pa + pq;
-                    pb[r] = to_bf16(pa);
-                    pb[4 + r] = to_bf16(pq);
-                }
-                // ---- O^T += C^T P^T over the 512 latent dims ----
-                {
-                    const char* pv_base = cur + pv_off + 32 * tb * DEC_ROW_STRIDE;
-                    constexpr int NS = kLatent / 16;
-                    auto rd = [&](int db) {
-                        return join(lds_read_tr16(pv_base, 32 * db),
-                                    lds_read_tr16(pv_base, 16 * DEC_ROW_STRIDE + 32 * db));
-                    };
-                    bf16x8 fv[DEC_PFV + 1];
-#pragma unroll
-                    for (int i = 0; i < DEC_PFV; ++i) fv[i] = rd(i);
-#pragma unroll
-                    for (int db = 0; db < NS; ++db) {
-                        if (db + DEC_PFV < NS) fv[(db + DEC_PFV) % (DEC_PFV + 1)] = rd(db + DEC_PFV);
-                        oacc[db] = mfma16(fv[db % (DEC_PFV + 1)], pb, oacc[db]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
+            for (int r = 0; r < 4; ++r) {
+                if (dec_token_of(g, r) >= valid) sa[r] = -INFINITY;
+                if (dec_token_of(g, 4 + r) >= valid) sb[r] = -INFINITY;
             }
         }
+        float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                         fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+        mt = max4_groups16(mt) * x.c_log2;
+        // Lazy rescale: the exponent base m only moves when some head's max
+        // exceeds it by more than kRescaleSlack (P stays below
+        // 2^kRescaleSlack); l and the accumulator share the base, so the
+        // final O = acc / l is unchanged.
+        if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < kLatent / 16; ++db) oacc[db] *= alpha;
+            m = m_new;
+        }
+        const float mb = (m == -INFINITY) ? 0.f : m;
+        bf16x8 pb;  // logical k = 8g + e
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pa = fast_exp2(__builtin_fmaf(sa[r], x.c_log2, -mb));
+            const float pq = fast_exp2(__builtin_fmaf(sb[r], x.c_log2, -mb));
+            l += pa + pq;
+            pb[r] = to_bf16(pa);
+            pb[4 + r] = to_bf16(pq);
+        }
+        return pb;
+    };
+
+    for (int j = 0; j < ntiles; ++j) {
+        char* cur = smem + (j % DEC_NBUF) * DEC_TILE_BYTES;
+        if (j + 1 < ntiles) dec_wait_tile<1>(w);   // tile j+1 may still be in flight
+        else wait_vmcnt<0>();
         lds_barrier();
+        if (j + DEC_AHEAD < ntiles)
+            dec_issue_tile(seq, len, tok_lo + (j + DEC_AHEAD) * DEC_TILE,
+                           smem + ((j + DEC_AHEAD) % DEC_NBUF) * DEC_TILE_BYTES, voff, w);
+        if (active) {
+            const uint32_t base = lds_addr(cur);
+            if (lag && j > 0) pv_phase(pv_prev, pb_prev);
+            const bf16x8 pb = qk_softmax(base + qk_off, tok_end - (tok_lo + j * DEC_TILE));
+            if (lag) {
+                pb_prev = pb;
+                pv_prev = base + pv_off;
+            } else {
+                pv_phase(base + pv_off, pb);
+            }
+        }
     }
+    if (active && lag && ntiles > 0) pv_phase(pv_prev, pb_prev);
+    lds_barrier();  // every wave is done with the ring before the next piece refills it
 
     if (!active) return;
     l = sum4_groups16(l);
     const float inv_l = 1.f / l;
     const float lse_v = (m + __builtin_log2f(l)) * kLn2;
     // O^T block db: lane (head n, g) holds dims 16db + 4g + 0..3.
-    const int ns = x.ws[x.a.seq_nsplit + b];
-    if (ns == 1) {
+    if (nsplit == 1) {
         __bf16* op = x.o + ((size_t)b * H + head) * kLatent + 4 * g;
 #pragma unroll
         for (int db = 0; db < kLatent / 16; ++db) {
@@ -368,7 +417,7 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
         // Partial of a split sequence: normalised over this piece, stored in
         // bf16 (the merge weights sum to one, so its rounding stays at the
         // level of the final bf16 output's).
-        const int slot = 2 * p + (x.ws[x.a.part_first_seq + p] == b ? 0 : 1);
+        const int slot = 2 * p + (first_in_part ? 0 : 1);
         __bf16* op = x.o_part + ((size_t)slot * H + head) * kLatent + 4 * g;
 #pragma unroll
         for (int db = 0; db < kLatent / 16; ++db) {
@@ -381,6 +430,11 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     }
 }
 
+// Pieces of part p, found without a chain of dependent loads: lane i reads
+// the plan entries of sequence b0 + i (b0 = the part's first sequence) in one
+// round trip, and a ballot lists the lanes whose sequence has tiles in the
+// part.  A part spans more than 64 sequences only when they are very short;
+// then the next 64 are read the same way.
 __global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int p = blockIdx.x;
@@ -391,16 +445,28 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) 
     const int whole = ws[kHdrMode];
     const int B = ws[kHdrB];
     const int pos_lo = p * t, pos_hi = pos_lo + t;
-    for (int b = ws[x.a.part_first_seq + p]; b < B; ++b) {
-        const int nb = ws[x.a.seq_n + b];
-        const int sb = ws[x.a.seq_start + b];
-        if (nb > 0) {
-            if (sb >= pos_hi) break;
-            const int lo = max(sb, pos_lo) - sb;
-            const int hi = min(sb + nb, pos_hi) - sb;
-            if (lo < hi) dec_piece(x, smem, p, b, lo, hi);
+    const int lane = lane_id();
+    const int b0 = ws[x.a.part_first_seq + p];
+    for (int base = b0; base < B; base += 64) {
+        const int b = base + lane;
+        int nb = 0, sb = pos_hi, ln = 0, ns = 0;
+        if (b < B && (!whole || b == b0)) {
+            nb = ws[x.a.seq_n + b];
+            sb = ws[x.a.seq_start + b];
+            ln = ws[x.a.seq_len + b];
+            ns = ws[x.a.seq_nsplit + b];
         }
-        if (whole) break;
+        const int lo = max(sb, pos_lo) - sb;
+        const int hi = min(sb + nb, pos_hi) - sb;
+        uint64_t pieces = __builtin_amdgcn_ballot_w64(nb > 0 && lo < hi);
+        const bool more = __builtin_amdgcn_ballot_w64(nb > 0 && sb >= pos_hi) == 0 && base + 64 < B && !whole;
+        while (pieces) {
+            const int i = __builtin_ctzll(pieces);
+            pieces &= pieces - 1;
+            dec_piece(x, smem, p, base + i, __builtin_amdgcn_readlane(lo, i), __builtin_amdgcn_readlane(hi, i),
+                      __builtin_amdgcn_readlane(ln, i), __builtin_amdgcn_readlane(ns, i), base + i == b0);
+        }
+        if (!more) break;
     }
 }
 
