@@ -15,7 +15,10 @@ prefill = bf16 causal prefill (B=4 H=16 N=4096 D=128) and the fp32
 cpu_baseline = the fp64 oracle on a bounded sample of the same decode
         workload, timed on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-prefill]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--no-cpu] [--no-prefill]
+
+The defaults warm up for 100 steps: the first few dozen decode calls after a
+start run 10-15% slower than the steady state (clock and cache ramp).
 """
 
 import argparse
@@ -37,8 +40,8 @@ METRIC = "MLA decode HBM GB/s (% of peak) + prefill attention TFLOPS (% MFMA pea
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32", "copy"], default=None,
@@ -120,7 +123,7 @@ def bench_decode(args, log):
                 absorb_bytes=absorb_bytes, plan=plan)
 
 
-def bench_prefill(log, name, causal, reps=10):
+def bench_prefill(log, name, causal, reps=None):
     import torch
     from mla_latent_kv_attn_amd import binding, workloads
     dev = "cuda:0"
@@ -129,10 +132,16 @@ def bench_prefill(log, name, causal, reps=10):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fn = lambda: binding.attn_fwd(q, k, v, w["scale"], causal, o=o, lse=lse)
-    for _ in range(3):
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(max(3, int(0.1 / est))):  # about 0.1 s of warm-up
         fn()
     torch.cuda.synchronize()
-    ms = time_events(fn, reps)
+    ms = time_events(fn, reps or max(10, min(100, int(0.2 / est))))
     avg = sum(ms) / len(ms)
     fl = attn_flops(w["B"], w["H"], w["N"], w["D"], causal)
     tf = fl / (avg * 1e-3) / 1e12

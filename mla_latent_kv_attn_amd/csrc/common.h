@@ -151,10 +151,60 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(uint32_t addr) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_u32x4(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+template <int OFF>
+__device__ __forceinline__ float ds_read_f32(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    float r;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// LDS writes in the same explicitly counted form (they count in lgkmcnt).
+template <int OFF>
+__device__ __forceinline__ void ds_write16(uint32_t addr, const bf16x8& v) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_write_f32(uint32_t addr, float v) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_write_u32(uint32_t addr, uint32_t v) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile("ds_write_b32 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
     static_assert(N >= 0 && N < 16, "lgkmcnt range");
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (N << 8) | (3 << 14));
+}
+
+// The same wait, written so that the values it guards (results of earlier
+// asm LDS reads) are operands of it: their consumers then depend on the wait
+// and cannot be scheduled ahead of it.  A bare waitcnt gives the compiler no
+// such dependency, and it does move arithmetic on asm results above it.
+template <int N, typename A>
+__device__ __forceinline__ void wait_lgkm_for(A& a) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a) : [n] "n"(N));
+}
+template <int N, typename A, typename B>
+__device__ __forceinline__ void wait_lgkm_for(A& a, B& b) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%[n])" : "+v"(a), "+v"(b) : [n] "n"(N));
 }
 
 // ---------------------------------------------------------------------------

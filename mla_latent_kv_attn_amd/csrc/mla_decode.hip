@@ -314,7 +314,7 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
             constexpr int db = decltype(db_c)::value;
             if constexpr (db + DEC_PFV < NS) rd_pv(std::integral_constant<int, db + DEC_PFV>{});
             constexpr int newer = 2 * ((NS - 1 - db) < DEC_PFV ? (NS - 1 - db) : DEC_PFV);
-            wait_lgkm<newer>();
+            wait_lgkm_for<newer>(fv[db % (DEC_PFV + 1)]);
             __builtin_amdgcn_sched_barrier(0);
             oacc[db] = mfma16(fv[db % (DEC_PFV + 1)], p, oacc[db]);
             __builtin_amdgcn_sched_barrier(0);
@@ -334,7 +334,7 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
             constexpr int kk = decltype(kk_c)::value;
             if constexpr (kk + DEC_PF < KS) rd_qk(std::integral_constant<int, kk + DEC_PF>{});
             constexpr int newer = 2 * ((KS - 1 - kk) < DEC_PF ? (KS - 1 - kk) : DEC_PF);
-            wait_lgkm<newer>();
+            wait_lgkm_for<newer>(fa[kk % (DEC_PF + 1)], fb[kk % (DEC_PF + 1)]);
             __builtin_amdgcn_sched_barrier(0);
             sa = mfma16(fa[kk % (DEC_PF + 1)], qf[kk], sa);
             sb = mfma16(fb[kk % (DEC_PF + 1)], qf[kk], sb);
