@@ -8,7 +8,12 @@
 //
 // Tiling (D = 128): a workgroup owns Br = 128 query rows of one (b, h);
 // wave w owns rows 32w..32w+31.  Key/value tiles of Bc = 64 rows are copied
-// global -> LDS (global_load_lds_dwordx4) into a double buffer.
+// global -> LDS (buffer_load_dwordx4 ... lds) into a double buffer.  Each
+// wave's per-lane source offsets within a tile are fixed; a tile only moves
+// the buffer base, and the buffer ends at key N - 1, so keys past N read as
+// zeros (and are masked).  LDS fragments are read with inline asm and waited
+// for with counted waits, so the next tile's copies stay in flight while the
+// current tile is computed.
 //
 // Products per wave and 64-key tile (v_mfma_f32_32x32x16_bf16):
 //   S^T = K Q^T  : A = K rows from LDS, B = Q held in VGPRs.  The result
@@ -23,7 +28,7 @@
 // current exponent base by more than kRescaleSlack.
 // Masks follow section 3.4: tiles past the causal limit are never loaded;
 // the element mask is applied only on tiles that straddle the diagonal; keys
-// past N are clamped on load and masked.  A tile whose keys are all masked
+// past N read as zeros and are masked.  A tile whose keys are all masked
 // for every row of a wave is skipped by that wave.
 #include "common.h"
 
@@ -40,8 +45,13 @@ constexpr int B16_TILE_BYTES = B16_BC * B16_STRIDE;                  // 17408
 constexpr int B16_TILE_INSTR = B16_BC * (B16_ROW_CHUNKS + 1) / 64;   // 17 wave-wide 1 KiB copies per tile
 static_assert(B16_BC * (B16_ROW_CHUNKS + 1) % 64 == 0, "whole copies");
 static_assert(B16_TILE_INSTR % B16_WAVES == 1, "wave 0 issues the one extra copy");
-constexpr int B16_LOADS_HI = 2 * ((B16_TILE_INSTR + B16_WAVES - 1) / B16_WAVES);  // K + V copies, wave 0
-constexpr int B16_LOADS_LO = 2 * (B16_TILE_INSTR / B16_WAVES);                    // other waves
+constexpr int B16_COPIES_HI = (B16_TILE_INSTR + B16_WAVES - 1) / B16_WAVES;  // copies per tile, wave 0
+constexpr int B16_COPIES_LO = B16_TILE_INSTR / B16_WAVES;                      // other waves
+constexpr int B16_LOADS_HI = 2 * B16_COPIES_HI;  // K + V copies, wave 0
+constexpr int B16_LOADS_LO = 2 * B16_COPIES_LO;  // other waves
+// LDS fragment prefetch distances (MFMA steps) of the score and PV loops.
+constexpr int B16_PF = 2;
+constexpr int B16_PFV = 3;
 
 // LDS rows have a stride of 16 (mod 128) bytes.  Inside each 32-key block
 // MFMA row rho = 16a + 8b + 4g + c is fed key 16a + 8b + g + 2c, so that
@@ -91,18 +101,29 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
 
     // Copy i (0..16) of 64 chunks of the K and of the V tile is issued by wave
     // i % 4.  Chunk L is row L / 17, chunk L % 17 (the pad chunk 16 repeats
-    // chunk 0).  Keys past N repeat key N-1 and are masked.
+    // chunk 0).  Copy k of this wave has the fixed per-lane source offset
+    // voff[k] within a tile.
+    uint32_t voff[B16_COPIES_HI];
+#pragma unroll
+    for (int kc = 0; kc < B16_COPIES_HI; ++kc) {
+        const int L = (w + B16_WAVES * kc) * 64 + lane;
+        const int r = L / (B16_ROW_CHUNKS + 1);
+        int c = L - r * (B16_ROW_CHUNKS + 1);
+        c = (c == B16_ROW_CHUNKS) ? 0 : c;
+        voff[kc] = (uint32_t)(r * B16_D * 2 + 16 * c);
+    }
     auto issue_tile = [&](int j, int buf) {
         const int kv_start = j * B16_BC;
-        for (int i = w; i < B16_TILE_INSTR; i += B16_WAVES) {
-            const int L = i * 64 + lane;
-            const int r = L / (B16_ROW_CHUNKS + 1);
-            int c = L - r * (B16_ROW_CHUNKS + 1);
-            c = (c == B16_ROW_CHUNKS) ? 0 : c;
-            const size_t grow = base + (size_t)min(kv_start + r, N - 1) * B16_D + 8 * c;
-            gload_lds16(k + grow, &smem[buf][0][i * 1024]);
-            gload_lds16(v + grow, &smem[buf][1][i * 1024]);
-        }
+        const uint32_t bytes = (uint32_t)(N - kv_start) * (uint32_t)(B16_D * 2);
+        const auto rk = make_rsrc(k + base + (size_t)kv_start * B16_D, bytes);
+        const auto rv = make_rsrc(v + base + (size_t)kv_start * B16_D, bytes);
+        static_for<B16_COPIES_HI>([&](auto kc_c) {
+            constexpr int kc = decltype(kc_c)::value;
+            if (kc < B16_COPIES_LO || w == 0) {
+                bload_lds16(rk, &smem[buf][0][(w + B16_WAVES * kc) * 1024], voff[kc]);
+                bload_lds16(rv, &smem[buf][1][(w + B16_WAVES * kc) * 1024], voff[kc]);
+            }
+        });
     };
 
     f32x16 oacc[B16_D / 32];
@@ -114,12 +135,20 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     float l = 0.f;        // this lane's share of the running sum
 
     // Per-lane LDS byte offsets (all other offsets are immediates).
-    const int k_off = b16_kappa32(n) * B16_STRIDE + 16 * g;
+    const uint32_t k_off = b16_kappa32(n) * B16_STRIDE + 16 * g;
     const int G = lane >> 4, sl = lane & 15;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
     const int jj = sl >> 2, qd = sl & 3;
-    const int v_off = ((G >> 1) + 2 * jj) * B16_STRIDE + 32 * (G & 1) + 8 * qd;
+    const uint32_t v_off = ((G >> 1) + 2 * jj) * B16_STRIDE + 32 * (G & 1) + 8 * qd;
+    const uint32_t smem_a = lds_addr(&smem[0][0][0]);
+    constexpr int KS = B16_D / 16;  // score k-steps
+    constexpr int PS = 16;          // PV steps: (ks, db) = (step / 4, step % 4)
 
     issue_tile(0, 0);
+    // The Q loads are older than tile 0's copies: wait for them here, so the
+    // loop body needs no wait on them (which would also stall on the next
+    // tile's copies).  One uniform count, so the compiler sees the wait on
+    // every path (wave 0 also waits for two of its tile-0 copies).
+    wait_vmcnt<B16_LOADS_LO>();
     for (int j = 0; j < Tc; ++j) {
         const int buf = j & 1;
         if (j + 1 < Tc) {
@@ -134,16 +163,39 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         const int kv_start = j * B16_BC;
         const bool wave_dead = CAUSAL && (kv_start > wrow0 + 31);
         if (!wave_dead) {
-            const char* Kt = smem[buf][0] + k_off;
-            const char* Vt = smem[buf][1] + v_off;
+            const uint32_t Kt = smem_a + buf * 2 * B16_TILE_BYTES + k_off;
+            const uint32_t Vt = smem_a + (buf * 2 + 1) * B16_TILE_BYTES + v_off;
+            // Score fragments: ring of B16_PF + 1 pairs (keys 0..31 and 32..63).
+            bf16x8 fa[B16_PF + 1], fb[B16_PF + 1];
+            auto rd_k = [&](auto kk_c) {
+                constexpr int kk = decltype(kk_c)::value;
+                fa[kk % (B16_PF + 1)] = ds_read16<32 * kk>(Kt);
+                fb[kk % (B16_PF + 1)] = ds_read16<32 * B16_STRIDE + 32 * kk>(Kt);
+            };
             f32x16 s0, s1;
 #pragma unroll
             for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-#pragma unroll
-            for (int kk = 0; kk < B16_D / 16; ++kk) {
-                s0 = mfma32(lds_read16(Kt, 32 * kk), qf[kk], s0);
-                s1 = mfma32(lds_read16(Kt, 32 * B16_STRIDE + 32 * kk), qf[kk], s1);
-            }
+            static_for<B16_PF>([&](auto i) { rd_k(i); });
+            static_for<KS>([&](auto kk_c) {
+                constexpr int kk = decltype(kk_c)::value;
+                if constexpr (kk + B16_PF < KS) rd_k(std::integral_constant<int, kk + B16_PF>{});
+                constexpr int newer = 2 * ((KS - 1 - kk) < B16_PF ? (KS - 1 - kk) : B16_PF);
+                wait_lgkm_for<newer>(fa[kk % (B16_PF + 1)], fb[kk % (B16_PF + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+                s0 = mfma32(fa[kk % (B16_PF + 1)], qf[kk], s0);
+                s1 = mfma32(fb[kk % (B16_PF + 1)], qf[kk], s1);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // The first V^T fragments are requested before the softmax so that
+            // its arithmetic covers their latency.
+            bf16x8 fv[B16_PFV + 1];
+            auto rd_v = [&](auto st_c) {
+                constexpr int st = decltype(st_c)::value;
+                constexpr int ks = st / 4, db = st % 4;
+                fv[st % (B16_PFV + 1)] = join(ds_read_tr16<16 * ks * B16_STRIDE + 64 * db>(Vt),
+                                              ds_read_tr16<(16 * ks + 8) * B16_STRIDE + 64 * db>(Vt));
+            };
+            static_for<B16_PFV>([&](auto i) { rd_v(i); });
             const bool tail = kv_start + B16_BC > N;
             const bool diag = CAUSAL && (kv_start + B16_BC - 1 > wrow0);
             if (tail || diag) {
@@ -182,15 +234,16 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                 pb[(e >> 3)][e & 7] = to_bf16(p0);
                 pb[2 + (e >> 3)][e & 7] = to_bf16(p1);
             }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int db = 0; db < B16_D / 32; ++db) {
-                    bf16x4 lo = lds_read_tr16(Vt, 16 * ks * B16_STRIDE + 64 * db);
-                    bf16x4 hi = lds_read_tr16(Vt, (16 * ks + 8) * B16_STRIDE + 64 * db);
-                    oacc[db] = mfma32(join(lo, hi), pb[ks], oacc[db]);
-                }
-            }
+            static_for<PS>([&](auto st_c) {
+                constexpr int st = decltype(st_c)::value;
+                constexpr int ks = st / 4, db = st % 4;
+                if constexpr (st + B16_PFV < PS) rd_v(std::integral_constant<int, st + B16_PFV>{});
+                constexpr int newer = 2 * ((PS - 1 - st) < B16_PFV ? (PS - 1 - st) : B16_PFV);
+                wait_lgkm_for<newer>(fv[st % (B16_PFV + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+                oacc[db] = mfma32(fv[st % (B16_PFV + 1)], pb[ks], oacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
         lds_barrier();
     }
