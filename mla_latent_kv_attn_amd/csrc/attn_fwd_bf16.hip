@@ -28,8 +28,7 @@
 // current exponent base by more than kRescaleSlack.
 // Masks follow section 3.4: tiles past the causal limit are never loaded;
 // the element mask is applied only on tiles that straddle the diagonal; keys
-// past N read as zeros and are masked.  A tile whose keys are all masked
-// for every row of a wave is skipped by that wave.
+// past N read as zeros and are masked.
 #include "common.h"
 
 namespace mla {
@@ -50,8 +49,14 @@ constexpr int B16_COPIES_LO = B16_TILE_INSTR / B16_WAVES;                      /
 constexpr int B16_LOADS_HI = 2 * B16_COPIES_HI;  // K + V copies, wave 0
 constexpr int B16_LOADS_LO = 2 * B16_COPIES_LO;  // other waves
 // LDS fragment prefetch distances (MFMA steps) of the score and PV loops.
-constexpr int B16_PF = 2;
-constexpr int B16_PFV = 3;
+#ifndef MLA_B16_PF
+#define MLA_B16_PF 2
+#endif
+#ifndef MLA_B16_PFV
+#define MLA_B16_PFV 3
+#endif
+constexpr int B16_PF = MLA_B16_PF;
+constexpr int B16_PFV = MLA_B16_PFV;
 
 // LDS rows have a stride of 16 (mod 128) bytes.  Inside each 32-key block
 // MFMA row rho = 16a + 8b + 4g + c is fed key 16a + 8b + g + 2c, so that
@@ -161,8 +166,11 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         lds_barrier();
 
         const int kv_start = j * B16_BC;
-        const bool wave_dead = CAUSAL && (kv_start > wrow0 + 31);
-        if (!wave_dead) {
+        // A tile entirely above this wave's rows (causal) is computed anyway:
+        // its scores are all masked, so it adds nothing, and the uniform
+        // control flow keeps the accumulators in place (a per-wave skip here
+        // makes the compiler copy them on every tile).
+        {
             const uint32_t Kt = smem_a + buf * 2 * B16_TILE_BYTES + k_off;
             const uint32_t Vt = smem_a + (buf * 2 + 1) * B16_TILE_BYTES + v_off;
             // Score fragments: ring of B16_PF + 1 pairs (keys 0..31 and 32..63).
@@ -196,6 +204,16 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                                               ds_read_tr16<(16 * ks + 8) * B16_STRIDE + 64 * db>(Vt));
             };
             static_for<B16_PFV>([&](auto i) { rd_v(i); });
+            // Tile max on the raw MFMA results (in the same block as the MFMAs,
+            // so the compiler knows them canonical and emits bare v_max3);
+            // only masked tiles recompute it after masking.
+            // (A sequential chain compiles to bare v_max3; nesting the pairwise
+            // max makes the compiler canonicalize every input first.)
+            float mt = s0[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s0[e]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s1[e]);
             const bool tail = kv_start + B16_BC > N;
             const bool diag = CAUSAL && (kv_start + B16_BC - 1 > wrow0);
             if (tail || diag) {
@@ -207,43 +225,56 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                     if (key >= lim) s0[e] = -INFINITY;
                     if (key + 32 >= lim) s1[e] = -INFINITY;
                 }
-            }
-            float mt = fmaxf(s0[0], s1[0]);
+                float mm = s0[0];
 #pragma unroll
-            for (int e = 1; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
+                for (int e = 1; e < 16; ++e) mm = fmaxf(mm, s0[e]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mm = fmaxf(mm, s1[e]);
+                mt = fminf(mt, mm);  // == mm; keeps the raw max in the MFMA block
+            }
             mt = max2_halves(mt) * c_log2;
+            // P = exp2(s c - base) in bf16 and this lane's row-sum share, then
+            // O^T += V^T P^T.  Written once per branch of the lazy rescale so
+            // that the common (no-rescale) path keeps the accumulators in place.
+            auto softmax_pv = [&]() {
+                const float mb = (m == -INFINITY) ? 0.f : m;
+                bf16x8 pb[4];  // k-step ks (keys 16ks..16ks+15 of the tile)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s0[e], c_log2, -mb));
+                    const float p1 = fast_exp2(__builtin_fmaf(s1[e], c_log2, -mb));
+                    l += p0 + p1;
+                    pb[(e >> 3)][e & 7] = to_bf16(p0);
+                    pb[2 + (e >> 3)][e & 7] = to_bf16(p1);
+                }
+                static_for<PS>([&](auto st_c) {
+                    constexpr int st = decltype(st_c)::value;
+                    constexpr int ks = st / 4, db = st % 4;
+                    if constexpr (st + B16_PFV < PS) rd_v(std::integral_constant<int, st + B16_PFV>{});
+                    constexpr int newer = 2 * ((PS - 1 - st) < B16_PFV ? (PS - 1 - st) : B16_PFV);
+                    wait_lgkm_for<newer>(fv[st % (B16_PFV + 1)]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    oacc[db] = mfma32(fv[st % (B16_PFV + 1)], pb[ks], oacc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
             // Lazy rescale (see kRescaleSlack): the base moves only when a
             // row max exceeds it by more than the slack.
             if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
                 const float m_new = fmaxf(m, mt);
                 const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
                 l *= alpha;
+                // In-place multiplies (each asm output tied to its input), so
+                // the accumulators keep their registers across this rare branch
+                // and the common path needs no copies.  The next reads of these
+                // registers are the PV MFMAs after the whole softmax.
 #pragma unroll
                 for (int db = 0; db < B16_D / 32; ++db)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+                    for (int e = 0; e < 16; ++e) asm("v_mul_f32_e32 %0, %1, %0" : "+v"(oacc[db][e]) : "v"(alpha));
                 m = m_new;
             }
-            const float mb = (m == -INFINITY) ? 0.f : m;
-            bf16x8 pb[4];  // k-step ks (keys 16ks..16ks+15 of the tile)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p0 = fast_exp2(__builtin_fmaf(s0[e], c_log2, -mb));
-                const float p1 = fast_exp2(__builtin_fmaf(s1[e], c_log2, -mb));
-                l += p0 + p1;
-                pb[(e >> 3)][e & 7] = to_bf16(p0);
-                pb[2 + (e >> 3)][e & 7] = to_bf16(p1);
-            }
-            static_for<PS>([&](auto st_c) {
-                constexpr int st = decltype(st_c)::value;
-                constexpr int ks = st / 4, db = st % 4;
-                if constexpr (st + B16_PFV < PS) rd_v(std::integral_constant<int, st + B16_PFV>{});
-                constexpr int newer = 2 * ((PS - 1 - st) < B16_PFV ? (PS - 1 - st) : B16_PFV);
-                wait_lgkm_for<newer>(fv[st % (B16_PFV + 1)]);
-                __builtin_amdgcn_sched_barrier(0);
-                oacc[db] = mfma32(fv[st % (B16_PFV + 1)], pb[ks], oacc[db]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+            softmax_pv();
         }
         lds_barrier();
     }
