@@ -18,22 +18,27 @@
 //   3. mla_combine_slots_kernel: log-sum-exp merge of the partials of every
 //      split sequence; also writes o = 0, lse = -inf for empty sequences.
 //
-// Split-kernel design.  A workgroup has 8 waves (two per SIMD); wave w owns
-// 16 heads, so one workgroup serves 128 heads and every cache byte crosses
-// HBM -> LDS once for all of them.  Per wave the q fragments (16 heads x
-// 576 bf16 = 72 VGPRs) and the fp32 output accumulator (16 x 512 = 128
-// VGPRs) stay in registers.  The cache streams through a ring of four
-// 32-token LDS tiles (4 x 37,888 B) filled by global_load_lds_dwordx4, so
-// three tiles (~111 KiB per CU) are in flight while one is computed: with a
-// single tile in flight the kernel is bound by memory latency, not by
-// bandwidth.  Per tile and wave (v_mfma_f32_16x16x32_bf16):
-//   S^T = C q^T   A = cache rows from LDS (K = 576 = 18 steps, two products
-//                 of 16 tokens), B = the wave's q fragments.  Tokens are fed
-//                 in a permuted order so that the S^T registers already form
-//                 the P^T operand of the PV product.
-//   O^T += C^T P^T  A = latent columns read transposed with
-//                 ds_read_b64_tr_b16 from the same LDS tile, B = P in bf16.
-// The same LDS bytes serve as key (576 dims) and value (first 512 dims).
+// Split-kernel design.  A workgroup is 4 waves, one per SIMD, and serves 128
+// heads, so every cache byte crosses HBM -> LDS once for all of them.  The
+// cache streams through a ring of four 32-token LDS tiles (37,888 B each)
+// filled by buffer_load ... lds.  Wave w owns heads 32w..32w+31 for the whole
+// computation:
+//   * their q fragments stay in VGPRs (32 heads x 576 bf16 = 144 VGPRs);
+//   * S^T = C q^T on v_mfma_f32_16x16x32_bf16, every cache fragment read from
+//     LDS feeding the MFMAs of both 16-head blocks;
+//   * online softmax (log2 domain, lazy rescale) in registers; P^T (bf16)
+//     stays in the registers that the value product reads;
+//   * O^T += C^T P^T with C^T read transposed (ds_read_b64_tr_b16) from the
+//     same tile; the 32 x 512 fp32 accumulators fill the 256 AGPRs.
+// Waves share nothing but the LDS tiles, so one barrier per tile suffices.
+// With one wave per SIMD there is no second wave to hide latency behind:
+// each tile step interleaves the value product of the previous tile with the
+// scores of the current one, and fragment reads run several MFMA groups
+// ahead, across the tile barrier where the tile is already resident.
+// The MFMAs are inline asm so that the score accumulators stay in VGPRs and
+// the value accumulators in fixed AGPRs.  The hardware interlocks
+// MFMA-to-MFMA accumulator chains; the places where ordinary instructions
+// read MFMA results carry explicit wait states (s_nop).
 #include <atomic>
 
 #include "common.h"
@@ -41,38 +46,29 @@
 
 namespace mla {
 
-constexpr int DEC_WAVES = 8;
-constexpr int DEC_HEADS = 16;  // heads per wave
+constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = DEC_WAVES * 64;
-static_assert(DEC_WAVES * DEC_HEADS == kDecodeHeadsPerWG, "head split");
+constexpr int DEC_HB = kDecodeHeadsPerWG / 16;                    // 8 head blocks of 16 per workgroup
 constexpr int DEC_ROW_CHUNKS = kRow * 2 / 16;                     // 72 chunks of 16 B per token
 constexpr int DEC_STRIDE_CHUNKS = DEC_ROW_CHUNKS + 2;             // +2 pad chunks per row in LDS
 constexpr int DEC_ROW_STRIDE = DEC_STRIDE_CHUNKS * 16;            // 1184 B (== 32 mod 128)
 constexpr int DEC_TILE = 32;                                      // tokens per LDS tile (one MFMA k-step of PV)
 constexpr int DEC_NBUF = 4;                                       // tiles in the LDS ring
-constexpr int DEC_AHEAD = DEC_NBUF - 2;                           // tiles in flight (one tile is computed, one
-                                                                  // kept for the lagging wave group's PV)
+constexpr int DEC_AHEAD = 2;                                      // tiles in flight (one more is held for values)
 constexpr int DEC_TILE_BYTES = DEC_TILE * DEC_ROW_STRIDE;         // 37888
 constexpr int DEC_TILE_INSTR = DEC_TILE * DEC_STRIDE_CHUNKS / 64; // 37 wave-wide 1 KiB copies per tile
-constexpr int DEC_SMEM = DEC_NBUF * DEC_TILE_BYTES;               // 151552
+constexpr int DEC_SMEM = DEC_NBUF * DEC_TILE_BYTES;               // 151,552 B
+static_assert(DEC_WAVES * 2 == DEC_HB, "two head blocks per wave");
 static_assert(DEC_TILE * DEC_STRIDE_CHUNKS % 64 == 0, "whole copies");
 static_assert(DEC_SMEM <= 160 * 1024, "LDS");
 static_assert(kDecodeTile % DEC_TILE == 0, "plan tiles are whole LDS tiles");
+static_assert(DEC_AHEAD + 2 <= DEC_NBUF, "ring: values tile, scores tile, tiles in flight");
 constexpr int DEC_LOADS_HI = (DEC_TILE_INSTR + DEC_WAVES - 1) / DEC_WAVES;  // copies of waves < EXTRA
 constexpr int DEC_LOADS_LO = DEC_TILE_INSTR / DEC_WAVES;                    // copies of the other waves
 constexpr int DEC_LOADS_EXTRA = DEC_TILE_INSTR % DEC_WAVES;                 // waves issuing one more copy
+static_assert(DEC_AHEAD * DEC_LOADS_HI < 64, "vmcnt range");
 
-// LDS fragment prefetch distances, in MFMA steps, for the S^T and PV loops.
-#ifndef MLA_DEC_PF_QK
-#define MLA_DEC_PF_QK 2
-#endif
-#ifndef MLA_DEC_PF_PV
-#define MLA_DEC_PF_PV 4
-#endif
-constexpr int DEC_PF = MLA_DEC_PF_QK;
-constexpr int DEC_PFV = MLA_DEC_PF_PV;
-static_assert(DEC_PF <= DEC_PFV, "PV ring slots 0..DEC_PF-1 are filled during the S^T tail");
-static_assert(2 * DEC_PF < 16 && 2 * DEC_PFV < 16, "lgkmcnt range");
+#define MLA_ALL_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191", "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207", "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223", "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239", "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
 
 struct PlanArgs {
     int seq_len, seq_n, seq_start, seq_first, seq_nsplit, part_first_seq;  // int32 offsets
@@ -85,7 +81,6 @@ struct PlanArgs {
 // 1168 or 1216 2x slower on gfx950); the transposed reads run at the same
 // rate for every stride tried.
 
-// ---------------------------------------------------------------------------
 // 1. Plan.  Cost line: sequence b occupies n_b + c0 positions (n_b tiles
 //    after c0 positions of fixed cost), empty sequences occupy none; part p
 //    owns positions [p t, (p+1) t) with
@@ -190,7 +185,7 @@ struct DecodeCtx {
 };
 
 // Copy one 32-token tile to LDS: copy i (0..36) of 64 chunks is issued by
-// wave i % 8.  Chunk L of the tile is row L / 74, chunk L % 74 of that row;
+// wave i % 4.  Chunk L of the tile is row L / 74, chunk L % 74 of that row;
 // the pad chunks (72, 73) receive second copies of chunks 0 and 1.  Each
 // wave's per-lane source offsets within a tile are fixed (dec_copy_offsets);
 // a tile only moves the buffer resource, whose size ends at the sequence's
@@ -206,22 +201,22 @@ __device__ __forceinline__ void dec_copy_offsets(uint32_t (&voff)[DEC_LOADS_HI],
     }
 }
 
-__device__ __forceinline__ void dec_issue_tile(const __bf16* seq, int len, int tok0, char* buf,
-                                               const uint32_t (&voff)[DEC_LOADS_HI], int w) {
-    const auto rsrc = make_rsrc(seq + (size_t)tok0 * kRow, (uint32_t)(len - tok0) * (uint32_t)(kRow * 2));
-    static_for<DEC_LOADS_HI>([&](auto k_c) {
-        constexpr int k = decltype(k_c)::value;
-        if (k < DEC_LOADS_LO || w < DEC_LOADS_EXTRA)
-            bload_lds16(rsrc, buf + (w + DEC_WAVES * k) * 1024, voff[k]);
-    });
-}
-
 // Wait until this wave's copies of the oldest in-flight tile have landed,
 // leaving `later` younger tiles in flight.
 template <int LATER>
 __device__ __forceinline__ void dec_wait_tile(int w) {
     if (w < DEC_LOADS_EXTRA) wait_vmcnt<LATER * DEC_LOADS_HI>();
     else wait_vmcnt<LATER * DEC_LOADS_LO>();
+}
+
+// Tile barrier.  Every wave has waited for its own copies of the tile that
+// becomes readable; LDS reads still in flight are fragment prefetches of the
+// previous tile, which no copy overwrites before the next barrier, so they
+// are not drained here.
+__device__ __forceinline__ void dec_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Token permutation inside a 32-token block, for v_mfma_f32_16x16x32_bf16.
@@ -237,205 +232,458 @@ __device__ __forceinline__ int dec_token_of(int g, int e) {  // e = 0..7 of lane
     return 16 * (e >> 2) + 2 * (e & 3) + (g & 1) + 8 * (g >> 1);
 }
 
+// Score MFMAs with VGPR accumulators.  mfma_v0: D = A B (C = 0); mfma_v:
+// D += A B.  Early-clobber on the first keeps D from overlapping the sources.
+__device__ __forceinline__ void mfma_v0(f32x4& d, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x4& d, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// The value accumulators live in fixed AGPRs: block k (= dim block * 2 +
+// head block) in a[4k .. 4k+3].  The compiler does not manage them at all
+// (it would keep VGPR copies of all 256 when any element is touched); every
+// access below names the registers itself, and acc_zero_all(), run at the
+// start of every piece, declares all 256 AGPRs clobbered so that the kernel
+// reserves them.
+__device__ __forceinline__ void acc_zero_all() {
+    asm volatile(
+        ".set .Lacc_i, 0\n\t"
+        ".rept 256\n\t"
+        "v_accvgpr_write_b32 a[.Lacc_i], 0\n\t"
+        ".set .Lacc_i, .Lacc_i + 1\n\t"
+        ".endr"
+        :
+        :
+        : MLA_ALL_AGPRS);
+}
+template <int K>
+__device__ __forceinline__ void acc_mfma(const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 a[%2:%3], %0, %1, a[%2:%3]" : : "v"(a), "v"(b), "i"(4 * K), "i"(4 * K + 3));
+}
+template <int K>
+__device__ __forceinline__ void acc_scale(float s) {  // a[4K..4K+3] *= s
+    float t0, t1, t2, t3;
+    asm volatile(
+        "v_accvgpr_read_b32 %0, a[%4]\n\tv_accvgpr_read_b32 %1, a[%5]\n\t"
+        "v_accvgpr_read_b32 %2, a[%6]\n\tv_accvgpr_read_b32 %3, a[%7]\n\t"
+        "v_mul_f32_e32 %0, %0, %8\n\tv_mul_f32_e32 %1, %1, %8\n\t"
+        "v_mul_f32_e32 %2, %2, %8\n\tv_mul_f32_e32 %3, %3, %8\n\t"
+        "v_accvgpr_write_b32 a[%4], %0\n\tv_accvgpr_write_b32 a[%5], %1\n\t"
+        "v_accvgpr_write_b32 a[%6], %2\n\tv_accvgpr_write_b32 a[%7], %3"
+        : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "i"(4 * K), "i"(4 * K + 1), "i"(4 * K + 2), "i"(4 * K + 3), "v"(s));
+}
+template <int K>
+__device__ __forceinline__ f32x4 acc_get() {
+    float t0, t1, t2, t3;
+    asm volatile(
+        "v_accvgpr_read_b32 %0, a[%4]\n\tv_accvgpr_read_b32 %1, a[%5]\n\t"
+        "v_accvgpr_read_b32 %2, a[%6]\n\tv_accvgpr_read_b32 %3, a[%7]"
+        : "=v"(t0), "=v"(t1), "=v"(t2), "=v"(t3)
+        : "i"(4 * K), "i"(4 * K + 1), "i"(4 * K + 2), "i"(4 * K + 3));
+    return f32x4{t0, t1, t2, t3};
+}
+// Wait states before ordinary instructions read registers that an MFMA just
+// wrote (more than the 16x16x32 bf16 MFMA's pass count needs).
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+// Max of a lane's eight scores of one head (two MFMA results), and the max
+// over the four lanes that hold the same head.  Written out because the
+// compiler canonicalises every operand of fmaxf that it did not produce
+// itself (one extra v_max per score).
+__device__ __forceinline__ float dec_max8(const f32x4& a, const f32x4& b) {
+    float t;
+    asm("v_max3_f32 %0, %1, %2, %3\n\t"
+        "v_max3_f32 %0, %0, %4, %5\n\t"
+        "v_max3_f32 %0, %0, %6, %7\n\t"
+        "v_max_f32_e32 %0, %0, %8"
+        : "=&v"(t)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+    return t;
+}
+__device__ __forceinline__ float dec_max_heads(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    float y;
+    asm("v_max_f32_e32 %0, %1, %2" : "=v"(y) : "v"(p[0]), "v"(p[1]));
+    u = __float_as_uint(y);
+    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    asm("v_max_f32_e32 %0, %1, %2" : "=v"(y) : "v"(q[0]), "v"(q[1]));
+    return y;
+}
+
+// Schedule of one tile step.  A step runs the value product of the previous
+// tile (32 dim blocks, "V" groups: two transposed reads and two MFMAs each)
+// and the scores of the current tile (18 k-steps, "K" groups: two reads and
+// four MFMAs each).  Group t's reads are issued DEC_D groups ahead, during
+// the MFMAs of group t - DEC_D.  A step with both products runs DEC_LEAD V
+// groups first (their reads are issued by the step before, across the tile
+// barrier, where that tile is already resident), then the 18 K groups with
+// DEC_NVK V groups spread evenly among them, then the remaining V groups,
+// over which the softmax of the tile is spread.  Steps without scores (the
+// last of a piece) or without values (the first) keep only the groups they
+// have.  The constants were chosen by measurement on MI355X (B=256, H=128,
+// varlen cache): prefetch 4 groups, 9 V groups among the K groups.
+constexpr int DEC_NK = kRow / 32;    // 18
+constexpr int DEC_NV = kLatent / 16; // 32
+constexpr int DEC_D = 4;
+constexpr int DEC_LEAD = 4;
+constexpr int DEC_NVK = 9;
+constexpr int DEC_SMX_AT = 1;        // softmax starts at the first MFMA of group last_k + 1
+static_assert(DEC_LEAD >= DEC_D && 2 * (DEC_D - 1) < 16, "prefetch across the barrier; lgkmcnt range");
+static_assert(DEC_LEAD + DEC_NVK <= DEC_NV, "V groups");
+// Fragment registers are named per group (one name per group of a step):
+// every read is a new value, so the names cost no registers, and the V
+// groups that one step prefetches for the next keep the names the next
+// step reads.
+constexpr int DEC_RK = DEC_NK;
+constexpr int DEC_RV = DEC_NV;
+
+struct DecTab {
+    int kind[DEC_NK + DEC_NV];
+    int idx[DEC_NK + DEC_NV];
+    int slot0[DEC_NK + DEC_NV];  // MFMA slots before group t
+    int kpos[DEC_NK + DEC_NV];   // K groups before group t
+    int n, last_k, nslots;
+};
+constexpr DecTab dec_make_tab(bool hk, bool hv) {
+    DecTab t{};
+    int n = 0, v = 0;
+    auto put = [&](int kind, int i) { t.kind[n] = kind; t.idx[n] = i; ++n; };
+    if (hk && hv) {
+        for (; v < DEC_LEAD; ++v) put(1, v);
+        for (int k = 0; k < DEC_NK; ++k) {
+            put(0, k);
+            t.last_k = n - 1;
+            for (const int target = DEC_LEAD + (k + 1) * DEC_NVK / DEC_NK; v < target; ++v) put(1, v);
+        }
+        for (; v < DEC_NV; ++v) put(1, v);
+    } else if (hk) {
+        for (int k = 0; k < DEC_NK; ++k) put(0, k);
+        t.last_k = n - 1;
+    } else {
+        for (; v < DEC_NV; ++v) put(1, v);
+        t.last_k = -1;
+    }
+    t.n = n;
+    int sl = 0, kp = 0;
+    for (int i = 0; i < n; ++i) {
+        t.slot0[i] = sl;
+        t.kpos[i] = kp;
+        sl += t.kind[i] == 0 ? 4 : 2;
+        kp += t.kind[i] == 0 ? 1 : 0;
+    }
+    t.nslots = sl;
+    return t;
+}
+template <bool HK, bool HV>
+struct DecSched {
+    static constexpr DecTab tab = dec_make_tab(HK, HV);
+    static constexpr int NG = tab.n;
+    static constexpr int kind(int t) { return tab.kind[t]; }
+    static constexpr int index(int t) { return tab.idx[t]; }
+    static constexpr int last_k() { return tab.last_k; }
+    static constexpr int slot0(int t) { return tab.slot0[t]; }
+    static constexpr int kpos(int t) { return tab.kpos[t]; }
+    static constexpr int nslots = tab.nslots;
+};
+
+struct DecState {
+    bf16x8 qf[2][DEC_NK];        // q fragments of the wave's two head blocks
+    bf16x8 fk[DEC_RK][2];        // K-group fragments (tokens 0..15 and 16..31)
+    bf16x4 fvl[DEC_RV], fvh[DEC_RV];  // V-group fragments (tokens 0..15 and 16..31)
+    bf16x8 pb[2];                // P^T of the previous tile, per head block
+    bf16x8 pnext[2];             // P^T of the current tile
+    float m[2], l[2], alpha[2];  // exponent base, row-sum share, pending rescale
+    bool resc;                   // a rescale is pending for the accumulators
+};
+
+// A workgroup whose head block is partial (H not a multiple of 128) computes
+// all eight 16-head blocks: missing heads get q = 0 and are never stored, so
+// the loops carry no head guards.
 __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile_lo, int tile_hi, int len,
                           int nsplit, bool first_in_part) {
     const int w = wave_id();
-    const int lane = lane_id();
+    // Redefined per piece so that lane-derived addresses are recomputed here
+    // instead of being hoisted out of the piece loop.
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));
     const int n = lane & 15;  // head column of the MFMA results / MFMA row of the A operand
     const int g = lane >> 4;  // row group (0..3)
     const int H = x.H;
-    const int hbase = blockIdx.y * kDecodeHeadsPerWG + DEC_HEADS * w;
-    const bool active = hbase < H;  // H % 16 == 0: a wave is fully in or out
-    const int head = hbase + n;
+    const int hblk = blockIdx.y * kDecodeHeadsPerWG;
+    const int nhb = min(DEC_HB, (H - hblk) >> 4);  // existing 16-head blocks (H % 16 == 0)
     const int tok_end = min(tile_hi * kDecodeTile, len);
-
-    f32x4 oacc[kLatent / 16];
-#pragma unroll
-    for (int db = 0; db < kLatent / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-
-    // Per-lane LDS byte offsets; everything else is a compile-time immediate.
-    const int qk_off = dec_pi16(n) * DEC_ROW_STRIDE + 16 * g;
-    const int jj = n >> 2, qd = n & 3;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
-    const int pv_off = dec_pi16(4 * g + jj) * DEC_ROW_STRIDE + 8 * qd;
-    // The piece covers plan tiles [tile_lo, tile_hi); LDS tiles are 32 tokens.
     const int tok_lo = tile_lo * kDecodeTile;
     const int ntiles = (tok_end - tok_lo + DEC_TILE - 1) / DEC_TILE;
 
-    // Ring of DEC_NBUF LDS tiles.  DEC_AHEAD tiles are in flight while tile j
-    // is computed, enough outstanding HBM reads per CU to cover the memory
-    // latency.  The two waves sharing a SIMD run half a tile apart: group A
-    // (waves 0-3) does S^T, softmax and PV of tile j; group B (waves 4-7)
-    // first finishes PV of tile j-1, then S^T and softmax of tile j, so one
-    // wave's softmax overlaps the other's matrix work.  One barrier per tile
-    // publishes tile j (every wave has waited for its own copies) and proves
-    // tile j-2 fully consumed, so tile j+DEC_AHEAD can be copied into its
-    // buffer right after it.
-    const bool lag = w >= DEC_WAVES / 2;
+    DecState st;
+    // q fragments (B operand of S^T = C q^T) of head blocks 2w and 2w+1: lane
+    // (head n, g) holds dims 32kk+8g..+7.  Missing heads read as zeros.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool act = 2 * w + h < nhb;
+        const size_t row = (size_t)b * H + hblk + 16 * (2 * w + h) + n;
+        const bf16x8* ql = reinterpret_cast<const bf16x8*>(x.q_lat + row * kLatent);
+        const bf16x8* qr = reinterpret_cast<const bf16x8*>(x.q_rope + row * kRope);
+#pragma unroll
+        for (int kk = 0; kk < kLatent / 32; ++kk) st.qf[h][kk] = act ? ql[4 * kk + g] : bf16x8{};
+#pragma unroll
+        for (int kk = 0; kk < kRope / 32; ++kk) st.qf[h][kLatent / 32 + kk] = act ? qr[4 * kk + g] : bf16x8{};
+    }
+
     const __bf16* seq = x.cache + (size_t)b * x.S_max * kRow;
     uint32_t voff[DEC_LOADS_HI];
     dec_copy_offsets(voff, w, lane);
+    // (the first DEC_AHEAD tiles are copied below, once tile_rsrc exists)
+
+    acc_zero_all();  // value accumulators: block (i, h) = dims 16i.., heads 16(2w+h)..
 #pragma unroll
-    for (int i = 0; i < DEC_AHEAD; ++i)
-        if (i < ntiles) dec_issue_tile(seq, len, tok_lo + i * DEC_TILE, smem + i * DEC_TILE_BYTES, voff, w);
+    for (int h = 0; h < 2; ++h) { st.m[h] = -INFINITY; st.l[h] = 0.f; st.alpha[h] = 1.f; }
+    st.resc = false;
 
-    // q fragments (loaded after the first tile copies are in flight) as the B
-    // operand of S^T = C q^T: lane (head n, g) holds dims 32kk+8g..+7.
-    bf16x8 qf[kRow / 32];
-    if (active) {
-        const bf16x8* ql = reinterpret_cast<const bf16x8*>(x.q_lat + ((size_t)b * H + head) * kLatent);
-        const bf16x8* qr = reinterpret_cast<const bf16x8*>(x.q_rope + ((size_t)b * H + head) * kRope);
-#pragma unroll
-        for (int kk = 0; kk < kLatent / 32; ++kk) qf[kk] = ql[4 * kk + g];
-#pragma unroll
-        for (int kk = 0; kk < kRope / 32; ++kk) qf[kLatent / 32 + kk] = qr[4 * kk + g];
-    }
+    // Per-lane LDS addresses; everything else is a compile-time immediate.
+    const uint32_t smem_a = lds_addr(smem);
+    const uint32_t qk_off = dec_pi16(n) * DEC_ROW_STRIDE + 16 * g;
+    const int jj = n >> 2, qd = n & 3;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
+    const uint32_t pv_off = dec_pi16(4 * g + jj) * DEC_ROW_STRIDE + 8 * qd;
 
-
-    constexpr int KS = kRow / 32;      // S^T k-steps
-    constexpr int NS = kLatent / 16;   // PV dim blocks
-    bf16x8 fa[DEC_PF + 1], fb[DEC_PF + 1], fv[DEC_PFV + 1];
-    bf16x8 pb_prev;                    // P of tile j-1 (lagging group)
-    uint32_t pv_prev = 0;              // LDS address of tile j-1's PV fragments
-
-    // Fragment rings: S^T fragments (fa, fb) run DEC_PF steps ahead of the
-    // MFMAs that consume them, PV fragments (fv) DEC_PFV steps.  Every S^T
-    // step issues one unit of two reads, so when step kk's pair is consumed
-    // exactly 2*DEC_PF newer reads are outstanding; PV step db has
-    // 2*min(DEC_PFV, NS-1-db).  Schedule barriers pin this order.
-    auto pv_phase = [&](uint32_t pv_a, const bf16x8& p) {
-        auto rd_pv = [&](auto db_c) {
-            constexpr int db = decltype(db_c)::value;
-            fv[db % (DEC_PFV + 1)] = join(ds_read_tr16<32 * db>(pv_a),
-                                          ds_read_tr16<16 * DEC_ROW_STRIDE + 32 * db>(pv_a));
-        };
-        static_for<DEC_PFV>([&](auto i) { rd_pv(i); });
-        static_for<NS>([&](auto db_c) {
-            constexpr int db = decltype(db_c)::value;
-            if constexpr (db + DEC_PFV < NS) rd_pv(std::integral_constant<int, db + DEC_PFV>{});
-            constexpr int newer = 2 * ((NS - 1 - db) < DEC_PFV ? (NS - 1 - db) : DEC_PFV);
-            wait_lgkm_for<newer>(fv[db % (DEC_PFV + 1)]);
-            __builtin_amdgcn_sched_barrier(0);
-            oacc[db] = mfma16(fv[db % (DEC_PFV + 1)], p, oacc[db]);
-            __builtin_amdgcn_sched_barrier(0);
-        });
+    // One fragment read: half 0 / 1 of group u of a step (tokens 0..15 / 16..31).
+    auto rd_k = [&](uint32_t qk_a, auto kk_c, auto half_c) {
+        constexpr int kk = decltype(kk_c)::value, half = decltype(half_c)::value;
+        st.fk[kk][half] = ds_read16<half * 16 * DEC_ROW_STRIDE + 64 * kk>(qk_a);
     };
-    // S^T for the tile's 32 tokens (sa: first 16, sb: second 16), masks,
-    // online softmax (log2 domain) and P in bf16.
-    auto qk_softmax = [&](uint32_t qk_a, int valid) -> bf16x8 {
-        auto rd_qk = [&](auto kk_c) {
-            constexpr int kk = decltype(kk_c)::value;
-            fa[kk % (DEC_PF + 1)] = ds_read16<64 * kk>(qk_a);
-            fb[kk % (DEC_PF + 1)] = ds_read16<16 * DEC_ROW_STRIDE + 64 * kk>(qk_a);
-        };
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-        static_for<DEC_PF>([&](auto i) { rd_qk(i); });
-        static_for<KS>([&](auto kk_c) {
-            constexpr int kk = decltype(kk_c)::value;
-            if constexpr (kk + DEC_PF < KS) rd_qk(std::integral_constant<int, kk + DEC_PF>{});
-            constexpr int newer = 2 * ((KS - 1 - kk) < DEC_PF ? (KS - 1 - kk) : DEC_PF);
-            wait_lgkm_for<newer>(fa[kk % (DEC_PF + 1)], fb[kk % (DEC_PF + 1)]);
-            __builtin_amdgcn_sched_barrier(0);
-            sa = mfma16(fa[kk % (DEC_PF + 1)], qf[kk], sa);
-            sb = mfma16(fb[kk % (DEC_PF + 1)], qf[kk], sb);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        if (valid < DEC_TILE) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (dec_token_of(g, r) >= valid) sa[r] = -INFINITY;
-                if (dec_token_of(g, 4 + r) >= valid) sb[r] = -INFINITY;
+    auto rd_v = [&](uint32_t pv_a, auto i_c, auto half_c) {
+        constexpr int i = decltype(i_c)::value, half = decltype(half_c)::value;
+        if constexpr (half == 0) st.fvl[i] = ds_read_tr16<32 * i>(pv_a);
+        else st.fvh[i] = ds_read_tr16<16 * DEC_ROW_STRIDE + 32 * i>(pv_a);
+    };
+
+    // One step: value product of the tile at pv_a (if HV), scores and softmax
+    // of the tile at qk_a (if HK), and (if HK and dma) the copies of a later
+    // tile into dst.  Each MFMA is followed by at most one other piece of
+    // work -- one fragment read, one copy, or one slice of the softmax -- so
+    // that it issues while the matrix pipe is busy: a wave issues in order,
+    // and reads bunched between two MFMAs hold the next MFMA back.  Group t
+    // issues the reads of group t + DEC_D after its first two MFMAs; on entry
+    // the first DEC_D groups' reads are in flight (issued by the previous
+    // step, or by the caller for the first), and a step with scores leaves
+    // the next step's first DEC_D groups (V groups of the tile at nv_a) in
+    // flight.
+    constexpr int NPIECE = 18;  // softmax slices: two for the max/rescale, sixteen exponentials
+    auto step = [&](auto hk_c, auto hv_c, uint32_t qk_a, uint32_t pv_a, uint32_t nv_a, int valid,
+                    __amdgpu_buffer_rsrc_t rsrc, char* dst) {
+        constexpr bool HK = decltype(hk_c)::value, HV = decltype(hv_c)::value;
+        using Sch = DecSched<HK, HV>;
+        constexpr int NG = Sch::NG;
+        if constexpr (HV) {
+            if (st.resc) {  // wave-uniform; the previous value product has finished
+                mfma_result_wait();
+                static_for<DEC_NV>([&](auto i_c) {
+                    constexpr int i = decltype(i_c)::value;
+                    acc_scale<2 * i>(st.alpha[0]);
+                    acc_scale<2 * i + 1>(st.alpha[1]);
+                });
+                asm volatile("s_nop 4");  // accumulator writes before the next MFMA reads them
             }
         }
-        float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
-                         fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-        mt = max4_groups16(mt) * x.c_log2;
-        // Lazy rescale: the exponent base m only moves when some head's max
-        // exceeds it by more than kRescaleSlack (P stays below
-        // 2^kRescaleSlack); l and the accumulator share the base, so the
-        // final O = acc / l is unchanged.
-        if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
-            const float m_new = fmaxf(m, mt);
-            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < kLatent / 16; ++db) oacc[db] *= alpha;
-            m = m_new;
-        }
-        const float mb = (m == -INFINITY) ? 0.f : m;
-        bf16x8 pb;  // logical k = 8g + e
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pa = fast_exp2(__builtin_fmaf(sa[r], x.c_log2, -mb));
-            const float pq = fast_exp2(__builtin_fmaf(sb[r], x.c_log2, -mb));
-            l += pa + pq;
-            pb[r] = to_bf16(pa);
-            pb[4 + r] = to_bf16(pq);
-        }
-        return pb;
-    };
+        f32x4 s[2][2];  // s[token half][head block]
+        float mt[2];    // the tile's max per head (log2 units)
 
-    for (int j = 0; j < ntiles; ++j) {
-        char* cur = smem + (j % DEC_NBUF) * DEC_TILE_BYTES;
-        if (j + 1 < ntiles) dec_wait_tile<1>(w);   // tile j+1 may still be in flight
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (j + DEC_AHEAD < ntiles)
-            dec_issue_tile(seq, len, tok_lo + (j + DEC_AHEAD) * DEC_TILE,
-                           smem + ((j + DEC_AHEAD) % DEC_NBUF) * DEC_TILE_BYTES, voff, w);
-        if (active) {
-            const uint32_t base = lds_addr(cur);
-            if (lag && j > 0) pv_phase(pv_prev, pb_prev);
-            const bf16x8 pb = qk_softmax(base + qk_off, tok_end - (tok_lo + j * DEC_TILE));
-            if (lag) {
-                pb_prev = pb;
-                pv_prev = base + pv_off;
+        auto issue_read = [&](auto u_c, auto half_c) {
+            constexpr int u = decltype(u_c)::value;
+            if constexpr (u < NG) {
+                if constexpr (Sch::kind(u) == 0) rd_k(qk_a, std::integral_constant<int, Sch::index(u)>{}, half_c);
+                else rd_v(pv_a, std::integral_constant<int, Sch::index(u)>{}, half_c);
+            } else if constexpr (HK) {
+                rd_v(nv_a, std::integral_constant<int, u - NG>{}, half_c);
+            }
+        };
+        auto piece = [&](auto p_c) {
+            constexpr int p = decltype(p_c)::value;
+            if constexpr (p == 0) {
+                mfma_result_wait();
+                if (valid < DEC_TILE) {  // the sequence's last tile; kept as a branch
+                    asm volatile("");
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (dec_token_of(g, r) >= valid) s[0][h][r] = -INFINITY;
+                            if (dec_token_of(g, 4 + r) >= valid) s[1][h][r] = -INFINITY;
+                        }
+                }
+                mt[0] = dec_max_heads(dec_max8(s[0][0], s[1][0])) * x.c_log2;
+            } else if constexpr (p == 1) {
+                mt[1] = dec_max_heads(dec_max8(s[0][1], s[1][1])) * x.c_log2;
+                const bool grow = (mt[0] > st.m[0] + kRescaleSlack) || (mt[1] > st.m[1] + kRescaleSlack);
+                // The base only moves when some head's max exceeds it by more
+                // than kRescaleSlack (always on the first tile, where m = -inf:
+                // every tile has at least one valid token, so the new base is
+                // finite and alpha = exp2(-inf) = 0); the accumulators are then
+                // scaled by alpha before the next value product.
+                st.resc = __builtin_amdgcn_ballot_w64(grow) != 0;
+                st.alpha[0] = st.alpha[1] = 1.f;
+                if (st.resc) {
+                    asm volatile("");
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float m_new = fmaxf(st.m[h], mt[h]);
+                        st.alpha[h] = fast_exp2(st.m[h] - m_new);
+                        st.l[h] *= st.alpha[h];
+                        st.m[h] = m_new;
+                    }
+                }
             } else {
-                pv_phase(base + pv_off, pb);
+                constexpr int q = p - 2, h = q >> 3, r = (q >> 1) & 3, half = q & 1;
+                const float e = fast_exp2(__builtin_fmaf(s[half][h][r], x.c_log2, -st.m[h]));
+                st.l[h] += e;
+                st.pnext[h][4 * half + r] = to_bf16(e);  // logical k = 8g + e
+            }
+        };
+        // Slot of the first softmax slice: the first MFMA of group
+        // last_k + DEC_SMX_AT (steps with values); steps without values run
+        // the softmax after their last MFMA.
+        constexpr int smx0 = HV && HK ? Sch::slot0(Sch::last_k() + DEC_SMX_AT) : 1 << 20;
+        static_assert(!(HV && HK) || smx0 + NPIECE <= Sch::nslots, "softmax slices fit in the step");
+
+        static_for<NG>([&](auto t_c) {
+            constexpr int t = decltype(t_c)::value;
+            constexpr int idx = Sch::index(t);
+            constexpr int kind = Sch::kind(t);
+            constexpr int nm = kind == 0 ? 4 : 2;
+            constexpr int newer = HK ? 2 * (DEC_D - 1) : 2 * (NG - 1 - t < DEC_D - 1 ? NG - 1 - t : DEC_D - 1);
+            if constexpr (kind == 0) wait_lgkm_for<newer>(st.fk[idx][0], st.fk[idx][1]);
+            else wait_lgkm_for<newer>(st.fvl[idx], st.fvh[idx]);
+            static_for<nm>([&](auto m_c) {
+                constexpr int m = decltype(m_c)::value;
+                if constexpr (kind == 0) {
+                    const bf16x8& f = st.fk[idx][m >> 1];
+                    const bf16x8& q = st.qf[m & 1][idx];
+                    f32x4& acc = s[m >> 1][m & 1];
+                    if constexpr (idx == 0) mfma_v0(acc, f, q);
+                    else mfma_v(acc, f, q);
+                } else {
+                    acc_mfma<2 * idx + m>(join(st.fvl[idx], st.fvh[idx]), st.pb[m]);
+                }
+                if constexpr (m < 2) {
+                    issue_read(std::integral_constant<int, t + DEC_D>{}, std::integral_constant<int, m>{});
+                } else if constexpr (HK) {
+                    constexpr int c = 2 * Sch::kpos(t) + (m - 2);  // copy number of this slot
+                    static_assert(kind == 0 && m >= 2 && c >= 0, "copies sit in the last two slots of K groups");
+                    if constexpr (c < DEC_LOADS_LO) {
+                        bload_lds16(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
+                    } else if constexpr (c < DEC_LOADS_HI) {
+                        if (w < DEC_LOADS_EXTRA) bload_lds16(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
+                    }
+                }
+                constexpr int p = Sch::slot0(t) + m - smx0;
+                if constexpr (p >= 0 && p < NPIECE) piece(std::integral_constant<int, p>{});
+                __builtin_amdgcn_sched_barrier(0);  // keep each slot's work in its place
+            });
+        });
+        if constexpr (HK && !HV) static_for<NPIECE>([&](auto p) { piece(p); });
+        if constexpr (HK) {
+            st.pb[0] = st.pnext[0];
+            st.pb[1] = st.pnext[1];
+        }
+    };
+
+    // Tile j is read as keys in step j and as values in step j + 1.  At the
+    // top of step j (< ntiles) every wave waits for its copies of tile j and
+    // passes the barrier; step j then copies tile j + 2 into the slot of tile
+    // j - 2, whose value product finished in step j - 1.
+    auto top = [&](int j) {
+        dec_wait_tile<1>(w);  // tile j has landed; tile j + 1 (real or empty) may still be in flight
+        dec_barrier();
+    };
+    auto tile_a = [&](int j) { return smem_a + (uint32_t)((j % DEC_NBUF) * DEC_TILE_BYTES); };
+    // Buffer of tile j's rows; a tile past the piece's end gets an empty
+    // buffer, whose copies write zeros into a slot that nothing reads, so the
+    // copies need no branch and the per-tile copy counts stay fixed.
+    auto tile_rsrc = [&](int j) {
+        const int tok0 = tok_lo + j * DEC_TILE;
+        const uint32_t bytes = j < ntiles ? (uint32_t)(len - tok0) * (uint32_t)(kRow * 2) : 0u;
+        return make_rsrc(seq + (size_t)(j < ntiles ? tok0 : 0) * kRow, bytes);
+    };
+
+#pragma unroll
+    for (int i = 0; i < DEC_AHEAD; ++i) {
+        const auto r = tile_rsrc(i);
+        static_for<DEC_LOADS_HI>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            if (k < DEC_LOADS_LO || w < DEC_LOADS_EXTRA) bload_lds16(r, smem + i * DEC_TILE_BYTES + (w + DEC_WAVES * k) * 1024, voff[k]);
+        });
+    }
+    top(0);
+    {
+        const uint32_t qa = tile_a(0) + qk_off;
+        static_for<DEC_D>([&](auto i) {
+            rd_k(qa, i, std::integral_constant<int, 0>{});
+            rd_k(qa, i, std::integral_constant<int, 1>{});
+        });
+        step(std::true_type{}, std::false_type{}, qa, 0u, tile_a(0) + pv_off, tok_end - tok_lo, tile_rsrc(DEC_AHEAD),
+             smem + (DEC_AHEAD % DEC_NBUF) * DEC_TILE_BYTES);
+    }
+    for (int j = 1; j < ntiles; ++j) {
+        top(j);
+        step(std::true_type{}, std::true_type{}, tile_a(j) + qk_off, tile_a(j - 1) + pv_off, tile_a(j) + pv_off,
+             tok_end - (tok_lo + j * DEC_TILE), tile_rsrc(j + DEC_AHEAD), smem + ((j + DEC_AHEAD) % DEC_NBUF) * DEC_TILE_BYTES);
+    }
+    step(std::false_type{}, std::true_type{}, 0u, tile_a(ntiles - 1) + pv_off, 0u, 0, tile_rsrc(0), smem);
+
+    // Normalise and store: O^T block (i, h) holds dims 16i + 4g + 0..3 of
+    // head 16(2w+h) + n.
+    mfma_result_wait();  // the accumulators are read below
+    static_for<2>([&](auto h_c) {
+        constexpr int h = decltype(h_c)::value;
+        const bool act = 2 * w + h < nhb;
+        const float lsum = sum4_groups16(st.l[h]);
+        const float il = 1.f / lsum;
+        const int head = hblk + 16 * (2 * w + h) + n;
+        if (act && g == 0) {
+            const float lse_v = (st.m[h] + __builtin_log2f(lsum)) * kLn2;
+            if (nsplit == 1) {
+                if (x.lse) x.lse[(size_t)b * H + head] = lse_v;
+            } else {
+                const int slot = 2 * p + (first_in_part ? 0 : 1);
+                x.lse_part[(size_t)slot * H + head] = lse_v;
             }
         }
-    }
-    if (active && lag && ntiles > 0) pv_phase(pv_prev, pb_prev);
-    lds_barrier();  // every wave is done with the ring before the next piece refills it
-
-    if (!active) return;
-    l = sum4_groups16(l);
-    const float inv_l = 1.f / l;
-    const float lse_v = (m + __builtin_log2f(l)) * kLn2;
-    // O^T block db: lane (head n, g) holds dims 16db + 4g + 0..3.
-    if (nsplit == 1) {
-        __bf16* op = x.o + ((size_t)b * H + head) * kLatent + 4 * g;
+        if (act) {
+            __bf16* obase;
+            if (nsplit == 1) {
+                obase = x.o + ((size_t)b * H + head) * kLatent;
+            } else {
+                const int slot = 2 * p + (first_in_part ? 0 : 1);
+                obase = x.o_part + ((size_t)slot * H + head) * kLatent;
+            }
+            obase += 4 * g;
+            static_for<DEC_NV>([&](auto i_c) {
+                constexpr int i = decltype(i_c)::value;
+                const f32x4 v = acc_get<2 * i + h>();
+                bf16x4 t;
 #pragma unroll
-        for (int db = 0; db < kLatent / 16; ++db) {
-            bf16x4 t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][r] * inv_l);
-            *reinterpret_cast<bf16x4*>(op + 16 * db) = t;
+                for (int r = 0; r < 4; ++r) t[r] = to_bf16(v[r] * il);
+                *reinterpret_cast<bf16x4*>(obase + 16 * i) = t;
+            });
         }
-        if (x.lse && g == 0) x.lse[(size_t)b * H + head] = lse_v;
-    } else {
-        // Partial of a split sequence: normalised over this piece, stored in
-        // bf16 (the merge weights sum to one, so its rounding stays at the
-        // level of the final bf16 output's).
-        const int slot = 2 * p + (first_in_part ? 0 : 1);
-        __bf16* op = x.o_part + ((size_t)slot * H + head) * kLatent + 4 * g;
-#pragma unroll
-        for (int db = 0; db < kLatent / 16; ++db) {
-            bf16x4 t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][r] * inv_l);
-            *reinterpret_cast<bf16x4*>(op + 16 * db) = t;
-        }
-        if (g == 0) x.lse_part[(size_t)slot * H + head] = lse_v;
-    }
+    });
+    // The next piece copies into slots that this piece's last value product
+    // read, and this piece's last (empty) copies must land first.
+    wait_vmcnt<0>();
+    lds_barrier();
 }
 
 // Pieces of part p, found without a chain of dependent loads: lane i reads
 // the plan entries of sequence b0 + i (b0 = the part's first sequence) in one
 // round trip, and a ballot lists the lanes whose sequence has tiles in the
-// part.  A part spans more than 64 sequences only when they are very short;
-// then the next 64 are read the same way.
-__global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) {
+// part.  Only the ballot mask stays live across pieces; each piece re-reads
+// its sequence's entries with scalar loads.  A part spans more than 64
+// sequences only when they are very short; then the next 64 are read the
+// same way.
+__global__ __launch_bounds__(DEC_THREADS, 1) void mla_split_kernel(DecodeCtx x) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int p = blockIdx.x;
     const int* ws = x.ws;
@@ -448,25 +696,27 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void mla_split_kernel(DecodeCtx x) 
     const int lane = lane_id();
     const int b0 = ws[x.a.part_first_seq + p];
     for (int base = b0; base < B; base += 64) {
-        const int b = base + lane;
-        int nb = 0, sb = pos_hi, ln = 0, ns = 0;
-        if (b < B && (!whole || b == b0)) {
-            nb = ws[x.a.seq_n + b];
-            sb = ws[x.a.seq_start + b];
-            ln = ws[x.a.seq_len + b];
-            ns = ws[x.a.seq_nsplit + b];
+        uint64_t pieces, more;
+        {
+            const int b = base + lane;
+            int nb = 0, sb = pos_hi;
+            if (b < B && (!whole || b == b0)) {
+                nb = ws[x.a.seq_n + b];
+                sb = ws[x.a.seq_start + b];
+            }
+            pieces = __builtin_amdgcn_ballot_w64(nb > 0 && max(sb, pos_lo) < min(sb + nb, pos_hi));
+            more = __builtin_amdgcn_ballot_w64(nb > 0 && sb >= pos_hi);
         }
-        const int lo = max(sb, pos_lo) - sb;
-        const int hi = min(sb + nb, pos_hi) - sb;
-        uint64_t pieces = __builtin_amdgcn_ballot_w64(nb > 0 && lo < hi);
-        const bool more = __builtin_amdgcn_ballot_w64(nb > 0 && sb >= pos_hi) == 0 && base + 64 < B && !whole;
         while (pieces) {
             const int i = __builtin_ctzll(pieces);
             pieces &= pieces - 1;
-            dec_piece(x, smem, p, base + i, __builtin_amdgcn_readlane(lo, i), __builtin_amdgcn_readlane(hi, i),
-                      __builtin_amdgcn_readlane(ln, i), __builtin_amdgcn_readlane(ns, i), base + i == b0);
+            const int b = base + i;  // uniform: plan entries come through the scalar cache
+            const int nb = ws[x.a.seq_n + b], sb = ws[x.a.seq_start + b];
+            const int ln = ws[x.a.seq_len + b], ns = ws[x.a.seq_nsplit + b];
+            const int lo = max(sb, pos_lo) - sb, hi = min(sb + nb, pos_hi) - sb;
+            dec_piece(x, smem, p, b, lo, hi, ln, ns, b == b0);
         }
-        if (!more) break;
+        if (more != 0 || base + 64 >= B || whole) break;
     }
 }
 
@@ -628,3 +878,4 @@ hipError_t launch_mla_combine(const float* o_part, const float* lse_part, __bf16
 }
 
 }  // namespace mla
+

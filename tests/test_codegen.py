@@ -1,0 +1,74 @@
+"""Generated-code checks for the decode split kernel (CPU only: hipcc
+cross-compiles gfx950 here).
+
+The kernel keeps its value accumulators in fixed AGPRs named by inline asm
+(a[4k .. 4k+3] for block k), which the compiler does not track.  That is only
+sound while the compiler itself allocates no AGPR and spills nothing: a
+compiler-chosen AGPR (an accumulator of a compiler MFMA, or a VGPR spilled to
+an AGPR) would silently overwrite accumulator state.  The inline asm always
+writes AGPRs in bracket form (a[N] or a[N:M]); the compiler prints single
+AGPRs bare (aN), so any bare AGPR operand in the kernel body is a
+compiler-allocated one.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from mla_latent_kv_attn_amd import build as B
+
+SRC = os.path.join(B.CSRC, "mla_decode.hip")
+KERNEL = "_ZN3mla16mla_split_kernelENS_9DecodeCtxE"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "mla_decode.s"
+    cmd = [B.HIPCC, *B.COMMON_FLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    return out.read_text()
+
+
+def kernel_body(text):
+    lines = text.splitlines()
+    start = next(i for i, l in enumerate(lines) if l.startswith(KERNEL + ":"))
+    end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
+    return [l.split(";")[0].strip() for l in lines[start:end]]
+
+
+def kernel_meta(text, key):
+    # per-kernel metadata entries start with "- .agpr_count"; pick the split kernel's
+    blocks = [b for b in re.split(r"\n\s+- \.agpr_count", text) if re.search(r"\.name:\s+" + re.escape(KERNEL) + r"\b", b)]
+    assert len(blocks) == 1, "kernel metadata missing"
+    v = re.findall(r"\." + key + r":\s+(\d+)", blocks[0])
+    assert v, key
+    return int(v[0])
+
+
+def test_no_compiler_allocated_agprs(asm):
+    bare = re.compile(r"(?<![\w\[:])a\d+\b")
+    offenders = []
+    for line in kernel_body(asm):
+        if not line or line.startswith(".") or line.endswith(":"):
+            continue
+        op, _, operands = line.partition(" ")
+        if bare.search(operands):
+            offenders.append(line)
+    assert not offenders, offenders[:5]
+
+
+def test_no_spills_or_scratch(asm):
+    assert kernel_meta(asm, "vgpr_spill_count") == 0
+    assert kernel_meta(asm, "sgpr_spill_count") == 0
+    m = re.search(KERNEL + r"\n(?:.*\n)*?\s+\.amdhsa_private_segment_fixed_size (\d+)", asm)
+    assert m and int(m.group(1)) == 0
+
+
+def test_one_step_of_each_kind(asm):
+    # the piece body holds exactly one first step (72 MFMAs), one middle step
+    # (136) and one last step (64): nothing is duplicated by the compiler
+    body = kernel_body(asm)
+    assert sum(1 for l in body if l.startswith("v_mfma")) == 72 + 136 + 64
