@@ -15,6 +15,13 @@
 // from the row-major slab, B = q_nope rows read straight from global memory
 // (16 contiguous bytes per lane), so each lane ends with 4 consecutive
 // latent columns of one row and stores them as 8 bytes.
+//
+// The Dl / 128 workgroups of one head read the same q_nope rows.  Work is
+// dealt to the 8 XCDs round-robin in dispatch order, so the block index is
+// mapped such that a head's column blocks are dispatched to one XCD, one
+// after another: the rows then come from that XCD's L2 after the first
+// read.  For Dn = 128 (the decode shape) the q_nope rows of the next block
+// of 64 are loaded while the current block's MFMAs run.
 #include "common.h"
 
 namespace mla {
@@ -24,59 +31,115 @@ constexpr int ABS_COLS = 128;
 
 __device__ __forceinline__ int abs_swz(int r) { return (r & 7) << 1; }
 
+// Block index -> (head, column block).  With H % 8 == 0, XCD x (= L % 8)
+// receives heads x, x + 8, ..., each head's column blocks consecutively.
+__device__ __forceinline__ void abs_block(int L, int H, int nc, int& h, int& cb) {
+    if ((H & 7) == 0) {
+        const int x = L & 7, k = L >> 3;
+        h = x + 8 * (k / nc);
+        cb = k - (k / nc) * nc;
+    } else {
+        h = L / nc;
+        cb = L - h * nc;
+    }
+}
+
+// W_UK[h][:, col0:col0+128] -> LDS, chunk p of row r stored at p ^ abs_swz(r).
+__device__ __forceinline__ void abs_load_w(const __bf16* w_uk, char* smem, int h, int col0, int Dn, int Dl, int w,
+                                           int lane) {
+    const __bf16* src = w_uk + (size_t)h * Dn * Dl + col0;
+    const int chunks = Dn * 16;
+    for (int c0 = w * 64; c0 < chunks; c0 += 4 * 64) {
+        const int L = c0 + lane;
+        const int r = L >> 4, p = L & 15;
+        gload_lds16(src + (size_t)r * Dl + 8 * (p ^ abs_swz(r)), smem + c0 * 16);
+    }
+}
+
+// acc[db] += W^T[cols 16db.., k-step kk] q^T for one k-step.
+__device__ __forceinline__ void abs_kstep(const char* smem, int kk, int g, int jj, int qd, const bf16x8& bq,
+                                          f32x4 (&acc)[ABS_COLS / 16]) {
+    const int r_lo = 32 * kk + 8 * g + jj, r_hi = r_lo + 4;
+#pragma unroll
+    for (int db = 0; db < ABS_COLS / 16; ++db) {
+        const int ch = 2 * db + (qd >> 1), half = (qd & 1) * 8;
+        bf16x4 lo = lds_read_tr16(smem, r_lo * 256 + ((ch ^ abs_swz(r_lo)) << 4) + half);
+        bf16x4 hi = lds_read_tr16(smem, r_hi * 256 + ((ch ^ abs_swz(r_hi)) << 4) + half);
+        acc[db] = mfma16(join(lo, hi), bq, acc[db]);
+    }
+}
+
+__device__ __forceinline__ void abs_store(__bf16* q_lat, const f32x4 (&acc)[ABS_COLS / 16], int b, int B, int H,
+                                          int h, int Dl, int col0, int g) {
+    if (b < B) {
+        __bf16* out = q_lat + ((size_t)b * H + h) * Dl + col0;
+#pragma unroll
+        for (int db = 0; db < ABS_COLS / 16; ++db) {
+            bf16x4 t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[db][r]);
+            *reinterpret_cast<bf16x4*>(out + 16 * db + 4 * g) = t;
+        }
+    }
+}
+
 __global__ __launch_bounds__(ABS_THREADS, 2) void mla_absorb_kernel(const __bf16* __restrict__ q_nope,
                                                                    const __bf16* __restrict__ w_uk,
                                                                    __bf16* __restrict__ q_lat, int B, int H,
                                                                    int Dn, int Dl) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [Dn][128] bf16, 256-byte rows
-    const int h = blockIdx.y;
-    const int col0 = blockIdx.x * ABS_COLS;
+    int h, cb;
+    abs_block(blockIdx.x, H, Dl / ABS_COLS, h, cb);
+    const int col0 = cb * ABS_COLS;
     const int w = wave_id();
     const int lane = lane_id();
+    const int n = lane & 15, g = lane >> 4;
+    const int jj = n >> 2, qd = n & 3;
+    auto qrow = [&](int bb) {
+        const int bl = min(bb + 16 * w + n, B - 1);
+        return reinterpret_cast<const bf16x8*>(q_nope + ((size_t)bl * H + h) * Dn);
+    };
 
-    // W_UK[h][:, col0:col0+128] -> LDS, chunk p of row r stored at p ^ abs_swz(r).
-    {
-        const __bf16* src = w_uk + (size_t)h * Dn * Dl + col0;
-        const int chunks = Dn * 16;
-        for (int c0 = w * 64; c0 < chunks; c0 += 4 * 64) {
-            const int L = c0 + lane;
-            const int r = L >> 4, p = L & 15;
-            gload_lds16(src + (size_t)r * Dl + 8 * (p ^ abs_swz(r)), smem + c0 * 16);
+    abs_load_w(w_uk, smem, h, col0, Dn, Dl, w, lane);
+    if (Dn == 128) {
+        // Rows of the first block are loaded with the slab; each block's
+        // MFMAs run while the next block's rows load.
+        constexpr int KS = 128 / 32;
+        bf16x8 cur[KS];
+        {
+            const bf16x8* q = qrow(0);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) cur[kk] = q[4 * kk + g];
         }
         wait_vmcnt<0>();
         __syncthreads();
+        for (int bb = 0; bb < B; bb += 64) {
+            bf16x8 nxt[KS];
+            if (bb + 64 < B) {
+                const bf16x8* q = qrow(bb + 64);
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) nxt[kk] = q[4 * kk + g];
+            }
+            f32x4 acc[ABS_COLS / 16];
+#pragma unroll
+            for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) abs_kstep(smem, kk, g, jj, qd, cur[kk], acc);
+            abs_store(q_lat, acc, bb + 16 * w + n, B, H, h, Dl, col0, g);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) cur[kk] = nxt[kk];
+        }
+        return;
     }
-
-    const int n = lane & 15, g = lane >> 4;
-    const int jj = n >> 2, qd = n & 3;
+    wait_vmcnt<0>();
+    __syncthreads();
     for (int bb = 0; bb < B; bb += 64) {
-        const int b = bb + 16 * w + n;
-        const int bl = min(b, B - 1);
-        const bf16x8* qrow = reinterpret_cast<const bf16x8*>(q_nope + ((size_t)bl * H + h) * Dn);
+        const bf16x8* q = qrow(bb);
         f32x4 acc[ABS_COLS / 16];
 #pragma unroll
         for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < Dn / 32; ++kk) {
-            const bf16x8 bq = qrow[4 * kk + g];
-            const int r_lo = 32 * kk + 8 * g + jj, r_hi = r_lo + 4;
-#pragma unroll
-            for (int db = 0; db < ABS_COLS / 16; ++db) {
-                const int ch = 2 * db + (qd >> 1), half = (qd & 1) * 8;
-                bf16x4 lo = lds_read_tr16(smem, r_lo * 256 + ((ch ^ abs_swz(r_lo)) << 4) + half);
-                bf16x4 hi = lds_read_tr16(smem, r_hi * 256 + ((ch ^ abs_swz(r_hi)) << 4) + half);
-                acc[db] = mfma16(join(lo, hi), bq, acc[db]);
-            }
-        }
-        if (b < B) {
-            __bf16* out = q_lat + ((size_t)b * H + h) * Dl + col0;
-#pragma unroll
-            for (int db = 0; db < ABS_COLS / 16; ++db) {
-                bf16x4 t;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[db][r]);
-                *reinterpret_cast<bf16x4*>(out + 16 * db + 4 * g) = t;
-            }
-        }
+        for (int kk = 0; kk < Dn / 32; ++kk) abs_kstep(smem, kk, g, jj, qd, q[4 * kk + g], acc);
+        abs_store(q_lat, acc, bb + 16 * w + n, B, H, h, Dl, col0, g);
     }
 }
 
@@ -89,7 +152,7 @@ hipError_t launch_mla_absorb(const __bf16* q_nope, const __bf16* w_uk, __bf16* q
         hipError_t e = ensure_smem_attr((const void*)mla_absorb_kernel, smem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(mla_absorb_kernel, dim3(Dl / ABS_COLS, H), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
+    hipLaunchKernelGGL(mla_absorb_kernel, dim3((Dl / ABS_COLS) * H), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
                        q_lat, B, H, Dn, Dl);
     return hipGetLastError();
 }
