@@ -96,6 +96,7 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
     const int tid = threadIdx.x;
     if (tid == 0) { s_max = 0; s_clamp = 0; s_carry = 0; }
     __syncthreads();
+    int my_n = 0, my_start = 0;  // sequence tid's entries (used when B <= 1024)
     for (int base = 0; base < B; base += 1024) {
         const int b = base + tid;
         int cost = 0;
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
             cost = n > 0 ? n + c0 : 0;
             ws[a.seq_len + b] = len;
             ws[a.seq_n + b] = n;
+            my_n = n;
             atomicMax(&s_max, n);
         }
         scan[tid] = cost;
@@ -117,7 +119,10 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
             scan[tid] += add;
             __syncthreads();
         }
-        if (b < B) ws[a.seq_start + b] = s_carry + scan[tid] - cost + c0;
+        if (b < B) {
+            my_start = s_carry + scan[tid] - cost + c0;
+            ws[a.seq_start + b] = my_start;
+        }
         __syncthreads();
         if (tid == 0) s_carry += scan[1023];
         __syncthreads();
@@ -139,8 +144,10 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
     for (int p = tid; p < nparts; p += 1024) ws[a.part_first_seq + p] = B;
     __syncthreads();
     for (int b = tid; b < B; b += 1024) {
-        const int n = ws[a.seq_n + b];
-        int start = ws[a.seq_start + b];
+        // With one chunk the entries are still in registers; otherwise they
+        // are read back (this thread wrote them above).
+        const int n = B <= 1024 ? my_n : ws[a.seq_n + b];
+        int start = B <= 1024 ? my_start : ws[a.seq_start + b];
         if (whole) {
             start = b * t + c0;
             ws[a.seq_start + b] = start;
@@ -746,9 +753,36 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
 template <typename PT, typename RowFn>
 __device__ __forceinline__ void combine_head(const PT* o_part, const float* lse_part, int nsplit, RowFn rows,
                                              __bf16* o_row, float* lse_out, int d8) {
-    float M = -INFINITY;
-#pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse_part[rows(s)]);
+    // One pass, four splits at a time: the loads of a chunk are independent
+    // and issued together; the running max M rescales what is summed so far.
+    float M = -INFINITY, W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        float ls[4], v[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            ls[k] = -INFINITY;
+            if (s0 + k < nsplit) {
+                const size_t r = rows(s0 + k);
+                ls[k] = lse_part[r];
+                load8(o_part + r * kLatent + 8 * d8, v[k]);
+            }
+        }
+        const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
+        if (m_new == -INFINITY) continue;  // every split so far is empty
+        const float sc = (M == -INFINITY) ? 0.f : __expf(M - m_new);
+        W *= sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= sc;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (ls[k] == -INFINITY) continue;  // empty split or past the end: weight 0
+            const float wgt = __expf(ls[k] - m_new);
+            W += wgt;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wgt, v[k][i], acc[i]);
+        }
+        M = m_new;
+    }
     bf16x8 out;
     if (M == -INFINITY) {
 #pragma unroll
@@ -756,18 +790,6 @@ __device__ __forceinline__ void combine_head(const PT* o_part, const float* lse_
         *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = out;
         if (lse_out && d8 == 0) *lse_out = -INFINITY;
         return;
-    }
-    float W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) {
-        const size_t r = rows(s);
-        const float ls = lse_part[r];
-        const float wgt = (ls == -INFINITY) ? 0.f : __expf(ls - M);
-        float v[8];
-        load8(o_part + r * kLatent + 8 * d8, v);
-        W += wgt;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = (wgt == 0.f) ? acc[i] : __builtin_fmaf(wgt, v[i], acc[i]);
     }
     const float inv = 1.f / W;
 #pragma unroll
@@ -789,11 +811,11 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine_slots_kernel(const in
     if (hh >= H) return;
     const int d8 = threadIdx.x & 63;
     const int first = ws[a.seq_first + b];
-    const int* pfs = ws + a.part_first_seq;
-    auto rows = [&](int s) -> size_t {
-        const int p = first + s;
-        return (size_t)(2 * p + (pfs[p] == b ? 0 : 1)) * H + hh;
-    };
+    // Part `first` may begin with an earlier sequence (then b's piece is in
+    // its second slot); every later part of b begins inside b, so b's piece
+    // there is in the part's first slot.
+    const int slot0 = 2 * first + (ws[a.part_first_seq + first] == b ? 0 : 1);
+    auto rows = [&](int s) -> size_t { return (size_t)(s == 0 ? slot0 : 2 * (first + s)) * H + hh; };
     combine_head(o_part, lse_part, ns, rows, o + ((size_t)b * H + hh) * kLatent,
                  lse ? lse + (size_t)b * H + hh : nullptr, d8);
 }
