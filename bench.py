@@ -119,8 +119,23 @@ def bench_decode(args, log):
     log(f"decode: {ms_step:.4f} ms/step wall, decode call {dec_avg*1e3:.1f} us, absorb {abs_avg*1e3:.1f} us, "
         f"parts_used={plan['parts_used']} t={plan['t']} max_nsplit={max(plan['nsplit'])}")
     absorb_bytes = (q_nope.numel() + w_uk.numel() + q_lat.numel()) * 2
+    # The value up-projection (o_v = o W_UV[h], 512 -> 128) is the step after
+    # the decode; it is timed on its own, outside the step.
+    w_uv = workloads.w_uv_weights(H=H).to(dev)
+    o_v = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+    for _ in range(10):
+        binding.mla_up_proj_v(o, w_uv, o_v=o_v)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(50):
+        binding.mla_up_proj_v(o, w_uv, o_v=o_v)
+    b.record(st)
+    b.synchronize()
+    up_ms = a.elapsed_time(b) / 50
+    up_bytes = (o.numel() + w_uv.numel() + o_v.numel()) * 2
+    log(f"value up-projection: {up_ms*1e3:.1f} us ({up_bytes/(up_ms*1e-3)/1e9:.0f} GB/s)")
     return dict(workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
-                absorb_bytes=absorb_bytes, plan=plan)
+                absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes)
 
 
 def bench_prefill(log, name, causal, reps=None):
@@ -277,6 +292,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(log),
                      "decode_us": round(d["dec_ms"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2)},
+        "value_up_projection": {"workload": "o [256,128,512] @ W_UV [128,512,128] -> [256,128,128] bf16",
+                                "us": round(d["up_ms"] * 1e3, 2),
+                                "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
+                                "note": "timed after the step, not part of value"},
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

@@ -92,8 +92,9 @@ size_t mla_decode_workspace_size(int B, int H, int num_splits);
  *   lse = natural log of sum_t exp(s_t)
  * No decompressed key or value is ever written.  The token range of each
  * sequence is split across compute units (at most num_splits pieces per
- * sequence) by an on-device planner; pieces write fp32 partials to the
- * workspace and a log-sum-exp combine merges them.  Three kernels are
+ * sequence) by an on-device planner; pieces write partials (bf16 outputs
+ * normalised by their own weight sum, fp32 LSE) to the workspace and a
+ * log-sum-exp combine merges them.  Three kernels are
  * enqueued (plan, split, combine); none waits on the host.
  *
  * q_lat    : [B, H, 512] bf16      q_rope : [B, H, 64] bf16
@@ -143,6 +144,24 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, void* o, fl
  */
 mla_status_t mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat,
                           int B, int H, int Dn, int Dl, hipStream_t stream);
+
+/*
+ * mla_up_proj_v - value up-projection of the latent decode output,
+ * [MLA-FA3 article] fused dataflow figure (the W_UK / W_UV projections of
+ * the in-place absorption stage):
+ *   o_v[b, h, :] = o_lat[b, h, :] @ W_UV[h]     (fp32 accumulation)
+ * Attention is linear in its values, so this equals attending over the
+ * explicitly decompressed values c^KV W_UV[h], without forming them.
+ * o_lat : [B, H, Dl] bf16 (e.g. the o of mla_decode_fwd, Dl = 512)
+ * w_uv  : [H, Dl, Dv] bf16 (per head: latent dim x value dim)
+ * o_v   : [B, H, Dv] bf16 (round to nearest even); written, never read.
+ * All buffers are device memory owned by the caller, 16-byte aligned.
+ * Sizes : B, H >= 1; Dl % 32 == 0, 32 <= Dl <= 512; Dv % 128 == 0,
+ *         128 <= Dv <= 4096; otherwise MLA_ERR_UNSUPPORTED / MLA_ERR_SHAPE,
+ *         and nothing is enqueued.
+ */
+mla_status_t mla_up_proj_v(const void* o_lat, const void* w_uv, void* o_v,
+                           int B, int H, int Dl, int Dv, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* mla_status_string(mla_status_t s);

@@ -14,6 +14,7 @@ __all__ = [
     "mla_decode_workspace_size",
     "mla_combine",
     "mla_absorb_q",
+    "mla_up_proj_v",
     "mla_status_string",
     "MlaError",
 ]

@@ -19,6 +19,7 @@ MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "mla_decode_workspace_size", "mla_decode_fwd", "mla_combine", "mla_absorb_q",
+            "mla_up_proj_v",
             "mla_status_string")
 
 
@@ -51,6 +52,8 @@ def load(path=None):
     lib.mla_combine.restype = i
     lib.mla_absorb_q.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.mla_absorb_q.restype = i
+    lib.mla_up_proj_v.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.mla_up_proj_v.restype = i
     lib.mla_status_string.argtypes = [i]
     lib.mla_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -179,6 +182,20 @@ def mla_absorb_q(q_nope, w_uk, q_lat=None):
     st = load().mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(q_lat), B, H, Dn, Dl, _stream(q_nope.device))
     _check("mla_absorb_q", st)
     return q_lat
+
+
+def mla_up_proj_v(o_lat, w_uv, o_v=None):
+    """o_v[b,h,:] = o_lat[b,h,:] @ w_uv[h]. o_lat [B,H,Dl] bf16, w_uv [H,Dl,Dv] bf16."""
+    B, H, Dl = o_lat.shape
+    Dv = w_uv.shape[2]
+    _need(o_lat, "o_lat", torch.bfloat16, (B, H, Dl))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, Dl, Dv))
+    if o_v is None:
+        o_v = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=o_lat.device)
+    _need(o_v, "o_v", torch.bfloat16, (B, H, Dv))
+    st = load().mla_up_proj_v(_ptr(o_lat), _ptr(w_uv), _ptr(o_v), B, H, Dl, Dv, _stream(o_lat.device))
+    _check("mla_up_proj_v", st)
+    return o_v
 
 
 def read_plan(workspace, B):

@@ -160,6 +160,18 @@ MLA_EXPORT mla_status_t mla_combine(const float* o_part, const float* lse_part, 
                                               stream));
 }
 
+// The value up-projection is the same per-head product as the absorption
+// (M = B, K = Dl, N = Dv) and runs on the same kernel.
+MLA_EXPORT mla_status_t mla_up_proj_v(const void* o_lat, const void* w_uv, void* o_v, int B, int H, int Dl, int Dv,
+                                      hipStream_t stream) {
+    if (!o_lat || !w_uv || !o_v) return MLA_ERR_NULL;
+    if (B < 1 || H < 1 || Dl < 1 || Dv < 1 || (long long)B * H > INT_MAX) return MLA_ERR_SHAPE;
+    if (Dl % 32 != 0 || Dl > 512 || Dv % 128 != 0 || Dv > 4096 || H > 65535) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(o_v)) return MLA_ERR_ALIGN;
+    return hip_status(mla::launch_mla_absorb(static_cast<const __bf16*>(o_lat), static_cast<const __bf16*>(w_uv),
+                                             static_cast<__bf16*>(o_v), B, H, Dl, Dv, stream));
+}
+
 MLA_EXPORT mla_status_t mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int B, int H, int Dn, int Dl,
                                      hipStream_t stream) {
     if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;

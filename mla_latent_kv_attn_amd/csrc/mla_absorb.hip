@@ -20,8 +20,10 @@
 // dealt to the 8 XCDs round-robin in dispatch order, so the block index is
 // mapped such that a head's column blocks are dispatched to one XCD, one
 // after another: the rows then come from that XCD's L2 after the first
-// read.  For Dn = 128 (the decode shape) the q_nope rows of the next block
-// of 64 are loaded while the current block's MFMAs run.
+// read.  When (head, column block) pairs alone would leave CUs idle (the
+// value up-projection has one 128-column block per head), the rows are
+// split into blocks as well.  For Dn = 128 and 512 the q_nope rows of the
+// next 64-row block are loaded while the current block's MFMAs run.
 #include "common.h"
 
 namespace mla {
@@ -31,17 +33,22 @@ constexpr int ABS_COLS = 128;
 
 __device__ __forceinline__ int abs_swz(int r) { return (r & 7) << 1; }
 
-// Block index -> (head, column block).  With H % 8 == 0, XCD x (= L % 8)
-// receives heads x, x + 8, ..., each head's column blocks consecutively.
-__device__ __forceinline__ void abs_block(int L, int H, int nc, int& h, int& cb) {
+// Block index -> (head, column block, row block).  With H % 8 == 0, XCD x
+// (= L % 8) receives heads x, x + 8, ..., each head's blocks consecutively.
+__device__ __forceinline__ void abs_block(int L, int H, int nc, int nb, int& h, int& cb, int& rb) {
+    const int units = nc * nb;
+    int k;
     if ((H & 7) == 0) {
-        const int x = L & 7, k = L >> 3;
-        h = x + 8 * (k / nc);
-        cb = k - (k / nc) * nc;
+        const int x = L & 7;
+        k = L >> 3;
+        h = x + 8 * (k / units);
     } else {
-        h = L / nc;
-        cb = L - h * nc;
+        h = L / units;
+        k = L;
     }
+    const int rem = k - (k / units) * units;
+    cb = rem % nc;
+    rb = rem / nc;
 }
 
 // W_UK[h][:, col0:col0+128] -> LDS, chunk p of row r stored at p ^ abs_swz(r).
@@ -83,14 +90,21 @@ __device__ __forceinline__ void abs_store(__bf16* q_lat, const f32x4 (&acc)[ABS_
     }
 }
 
-__global__ __launch_bounds__(ABS_THREADS, 2) void mla_absorb_kernel(const __bf16* __restrict__ q_nope,
+// KS > 0: Dn = 32 KS, and each row block's q_nope rows are loaded while the
+// previous block's MFMAs run.  KS == 0: any Dn, rows loaded per k-step.
+// (A 512-row slab fills 128 KiB of LDS: one workgroup per CU, so that
+// instance may use the whole register file.)
+template <int KS>
+__global__ __launch_bounds__(ABS_THREADS, KS == 16 ? 1 : 2) void mla_absorb_kernel(const __bf16* __restrict__ q_nope,
                                                                    const __bf16* __restrict__ w_uk,
                                                                    __bf16* __restrict__ q_lat, int B, int H,
-                                                                   int Dn, int Dl) {
+                                                                   int Dn, int Dl, int rows) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [Dn][128] bf16, 256-byte rows
-    int h, cb;
-    abs_block(blockIdx.x, H, Dl / ABS_COLS, h, cb);
+    const int nb = (B + rows - 1) / rows;
+    int h, cb, rb;
+    abs_block(blockIdx.x, H, Dl / ABS_COLS, nb, h, cb, rb);
     const int col0 = cb * ABS_COLS;
+    const int b_lo = rb * rows, b_hi = min(B, b_lo + rows);
     const int w = wave_id();
     const int lane = lane_id();
     const int n = lane & 15, g = lane >> 4;
@@ -101,21 +115,18 @@ __global__ __launch_bounds__(ABS_THREADS, 2) void mla_absorb_kernel(const __bf16
     };
 
     abs_load_w(w_uk, smem, h, col0, Dn, Dl, w, lane);
-    if (Dn == 128) {
-        // Rows of the first block are loaded with the slab; each block's
-        // MFMAs run while the next block's rows load.
-        constexpr int KS = 128 / 32;
+    if constexpr (KS > 0) {
         bf16x8 cur[KS];
         {
-            const bf16x8* q = qrow(0);
+            const bf16x8* q = qrow(b_lo);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) cur[kk] = q[4 * kk + g];
         }
         wait_vmcnt<0>();
         __syncthreads();
-        for (int bb = 0; bb < B; bb += 64) {
+        for (int bb = b_lo; bb < b_hi; bb += 64) {
             bf16x8 nxt[KS];
-            if (bb + 64 < B) {
+            if (bb + 64 < b_hi) {
                 const bf16x8* q = qrow(bb + 64);
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) nxt[kk] = q[4 * kk + g];
@@ -125,36 +136,59 @@ __global__ __launch_bounds__(ABS_THREADS, 2) void mla_absorb_kernel(const __bf16
             for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) abs_kstep(smem, kk, g, jj, qd, cur[kk], acc);
-            abs_store(q_lat, acc, bb + 16 * w + n, B, H, h, Dl, col0, g);
+            abs_store(q_lat, acc, bb + 16 * w + n, b_hi, H, h, Dl, col0, g);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) cur[kk] = nxt[kk];
         }
-        return;
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    for (int bb = 0; bb < B; bb += 64) {
-        const bf16x8* q = qrow(bb);
-        f32x4 acc[ABS_COLS / 16];
+    } else {
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int bb = b_lo; bb < b_hi; bb += 64) {
+            const bf16x8* q = qrow(bb);
+            f32x4 acc[ABS_COLS / 16];
 #pragma unroll
-        for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < Dn / 32; ++kk) abs_kstep(smem, kk, g, jj, qd, q[4 * kk + g], acc);
-        abs_store(q_lat, acc, bb + 16 * w + n, B, H, h, Dl, col0, g);
+            for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < Dn / 32; ++kk) abs_kstep(smem, kk, g, jj, qd, q[4 * kk + g], acc);
+            abs_store(q_lat, acc, bb + 16 * w + n, b_hi, H, h, Dl, col0, g);
+        }
     }
 }
 
 hipError_t ensure_smem_attr(const void* fn, int bytes);
 
-hipError_t launch_mla_absorb(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
+// Rows of q_nope per workgroup: all of them when the (head, column block)
+// grid alone fills the chip; otherwise split into row blocks (multiples of
+// 64) until about 256 workgroups run.
+static int abs_rows(int B, int H, int nc) {
+    const int blocks64 = (B + 63) / 64;
+    const long long units = (long long)H * nc;
+    int nb = units >= 256 ? 1 : (int)((256 + units - 1) / units);
+    nb = nb < 1 ? 1 : (nb > blocks64 ? blocks64 : nb);
+    return 64 * ((blocks64 + nb - 1) / nb);
+}
+
+template <int KS>
+static hipError_t launch_abs(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
                              hipStream_t stream) {
     const int smem = Dn * ABS_COLS * 2;
     if (smem > 64 * 1024) {
-        hipError_t e = ensure_smem_attr((const void*)mla_absorb_kernel, smem);
+        hipError_t e = ensure_smem_attr((const void*)mla_absorb_kernel<KS>, smem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(mla_absorb_kernel, dim3((Dl / ABS_COLS) * H), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
-                       q_lat, B, H, Dn, Dl);
+    const int nc = Dl / ABS_COLS;
+    const int rows = abs_rows(B, H, nc);
+    const long long grid = (long long)nc * H * ((B + rows - 1) / rows);
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(mla_absorb_kernel<KS>, dim3((unsigned)grid), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
+                       q_lat, B, H, Dn, Dl, rows);
     return hipGetLastError();
+}
+
+hipError_t launch_mla_absorb(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
+                             hipStream_t stream) {
+    if (Dn == 128) return launch_abs<4>(q_nope, w_uk, q_lat, B, H, Dn, Dl, stream);
+    if (Dn == 512) return launch_abs<16>(q_nope, w_uk, q_lat, B, H, Dn, Dl, stream);
+    return launch_abs<0>(q_nope, w_uk, q_lat, B, H, Dn, Dl, stream);
 }
 
 }  // namespace mla

@@ -105,6 +105,13 @@ def mla_varlen_workload(seed=1005, B=256, H=128, Dn=128, lo=256, hi=8192, S_max=
                 B=B, H=H, Dn=Dn, S_max=S_max, scale=1.0 / math.sqrt(ROW), seed=seed)
 
 
+def w_uv_weights(H=128, Dl=LATENT, Dv=128, seed=1006):
+    """Value up-projection weights W_UV [H, Dl, Dv], N(0, 0.02^2), bf16, from a
+    stream of their own (so the decode workload's draws are unchanged)."""
+    g = _gen(seed)
+    return (torch.randn((H, Dl, Dv), generator=g, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+
+
 def random_seqlens(B, lo, hi, seed):
     """Integer lengths uniform in [lo, hi] (inclusive) from their own stream."""
     g = _gen(seed)

@@ -25,11 +25,23 @@ Readings of what the pages leave open (each also listed in the design notes):
     never read; len_b = 0 gives O = 0 and LSE = -inf;
   * LSE is the natural log of the sum of exponentiated scaled scores.
 
+The value up-projection W_UV (named with W_UK in the article's fused
+dataflow figure, in the in-place absorption stage) maps the latent output to
+the per-head value space: o_v[b, h] = O[b, h] W_UV[h].  Because attention is
+linear in the values, applying it after the softmax-weighted sum equals
+attending over explicitly decompressed values V_h = c^KV W_UV[h]; that is the
+value-side counterpart of the absorption equation.  W_UV is laid out
+[H, 512, Dv] (per head, latent dim x value dim), the row-vector form of the
+column-vector W^UV blocks.
+
 Pinned by (tests/test_oracle_mla.py): pure-Python brute force on tiny
 inputs, identical cache rows (O = latent row, LSE = s + ln len), len = 1,
 the absorption identity against explicit decompression (sampled), decode
 through explicit decompression versus the absorbed decode, split invariance of
-the combine over arbitrary split plans, and combine closed forms.
+the combine over arbitrary split plans, combine closed forms; for the value
+up-projection, attention over explicitly decompressed values versus the
+latent output projected afterwards, a selection matrix (exact copy of chosen
+latent dims), and pure-Python loops on tiny inputs.
 """
 
 import numpy as np
@@ -43,6 +55,9 @@ __all__ = [
     "mla_decode_explicit_ref",
     "split_partials_ref",
     "combine_ref",
+    "up_project_v_ref",
+    "decompress_v_ref",
+    "mla_decode_values_explicit_ref",
 ]
 
 LATENT_DIM = 512
@@ -194,3 +209,58 @@ def combine_ref(o_part, lse_part):
     frac = np.where(alive, w / np.where(alive, tot, 1.0), 0.0)
     O = np.einsum("bhs,bhsd->bhd", frac, o_part)
     return O, LSE
+
+
+def up_project_v_ref(o_lat, w_uv):
+    """Value up-projection of the latent output: o_v[b, h, :] = O[b, h, :] @ W_UV[h].
+
+    o_lat [B, H, Dl], w_uv [H, Dl, Dv] -> [B, H, Dv] float64.
+    ([MLA-FA3 article] fused dataflow figure: the W_UK / W_UV projections of
+    the in-place absorption stage; here the W_UV one, applied once per query
+    after the softmax-weighted sum over the latent cache.)
+    """
+    o_lat, w_uv = _f64(o_lat), _f64(w_uv)
+    B, H, _ = o_lat.shape
+    out = np.empty((B, H, w_uv.shape[2]))
+    for h in range(H):
+        out[:, h, :] = o_lat[:, h, :] @ w_uv[h]
+    return out
+
+
+def decompress_v_ref(c_latent, w_uv):
+    """Explicit value decompression (the step the latent path avoids).
+
+    c_latent [T, 512], w_uv [H, 512, Dv] -> V [T, H, Dv] with
+    V[t, h, :] = c_t W_UV[h].
+    """
+    c_latent, w_uv = _f64(c_latent), _f64(w_uv)
+    T = c_latent.shape[0]
+    H, _, Dv = w_uv.shape
+    V = np.empty((T, H, Dv))
+    for h in range(H):
+        V[:, h, :] = c_latent @ w_uv[h]
+    return V
+
+
+def mla_decode_values_explicit_ref(q_lat, q_rope, w_uv, cache, seqlens, scale):
+    """Decode whose values are explicitly decompressed, V_h = c^KV W_UV[h].
+
+    Scores as in ``mla_decode_ref``; output o_v[b, h] = softmax(s) V_h.
+    Equal to up_project_v_ref(mla_decode_ref(...)[0], w_uv) up to rounding
+    (attention is linear in its values).  Returns o_v [B, H, Dv] (zeros for
+    an empty sequence).
+    """
+    q_lat, q_rope, cache, w_uv = _f64(q_lat), _f64(q_rope), _f64(cache), _f64(w_uv)
+    B, H, Dl = q_lat.shape
+    out = np.zeros((B, H, w_uv.shape[2]))
+    for b in range(B):
+        L = int(seqlens[b])
+        if L == 0:
+            continue
+        Q = np.concatenate([q_lat[b], q_rope[b]], axis=1)
+        C = cache[b, :L]
+        m, E, l = _softmax_rows(scale * (Q @ C.T))
+        P = E / l                                           # [H, L]
+        V = decompress_v_ref(C[:, :Dl], w_uv)               # [L, H, Dv]
+        out[b] = np.einsum("ht,thd->hd", P, V)
+    return out

@@ -99,6 +99,16 @@ def test_combine_and_absorb_validation_codes(lib):
     assert lib.mla_absorb_q(BAD, P, P, 4, 8, 128, 512, None) == binding.MLA_ERR_ALIGN
 
 
+def test_up_proj_validation_codes(lib):
+    assert lib.mla_up_proj_v(None, P, P, 4, 8, 512, 128, None) == binding.MLA_ERR_NULL
+    assert lib.mla_up_proj_v(P, P, None, 4, 8, 512, 128, None) == binding.MLA_ERR_NULL
+    assert lib.mla_up_proj_v(P, P, P, 4, 0, 512, 128, None) == binding.MLA_ERR_SHAPE
+    assert lib.mla_up_proj_v(P, P, P, 4, 8, 1024, 128, None) == binding.MLA_ERR_UNSUPPORTED
+    assert lib.mla_up_proj_v(P, P, P, 4, 8, 500, 128, None) == binding.MLA_ERR_UNSUPPORTED
+    assert lib.mla_up_proj_v(P, P, P, 4, 8, 512, 100, None) == binding.MLA_ERR_UNSUPPORTED
+    assert lib.mla_up_proj_v(P, P, BAD, 4, 8, 512, 128, None) == binding.MLA_ERR_ALIGN
+
+
 def test_workspace_size_rejects_bad_shapes(lib):
     assert lib.mla_decode_workspace_size(0, 128, 4) == 0
     assert lib.mla_decode_workspace_size(4, 17, 4) == 0

@@ -159,6 +159,43 @@ def test_absorb_shapes(B, H, Dn, Dl):
     assert rel <= 4e-3
 
 
+def test_up_proj_full_shape():
+    # The value up-projection at the decode shape: o_lat [256,128,512] @ W_UV [128,512,128].
+    g = torch.Generator().manual_seed(2006)
+    o_lat = torch.randn((256, 128, 512), generator=g).to(torch.bfloat16)
+    w_uv = workloads.w_uv_weights()
+    o_v = binding.mla_up_proj_v(o_lat.to(DEV), w_uv.to(DEV))
+    sync()
+    ref = OM.up_project_v_ref(np64(o_lat), np64(w_uv))
+    mx, rel = check_bf16(o_v, ref, "o_v 256x128x512->128")
+    assert rel <= 4e-3          # bf16 output rounding only
+
+
+@pytest.mark.parametrize("B,H,Dl,Dv", [(1, 1, 32, 128), (7, 3, 512, 256), (65, 2, 256, 128)])
+def test_up_proj_shapes(B, H, Dl, Dv):
+    g = torch.Generator().manual_seed(B * 100 + Dl)
+    o_lat = torch.randn((B, H, Dl), generator=g).to(torch.bfloat16)
+    w = (torch.randn((H, Dl, Dv), generator=g) * 0.05).to(torch.bfloat16)
+    o_v = binding.mla_up_proj_v(o_lat.to(DEV), w.to(DEV))
+    sync()
+    mx, rel = check_bf16(o_v, OM.up_project_v_ref(np64(o_lat), np64(w)), f"o_v {B}x{H}x{Dl}x{Dv}")
+    assert rel <= 4e-3
+
+
+def test_decode_then_up_proj_equals_attention_over_decompressed_values():
+    # Latent decode, then W_UV, on the GPU, against the oracle's attention
+    # over explicitly decompressed values c W_UV[h] (never formed on the GPU).
+    B, H, lens, S_max = 3, 128, [300, 77, 1], 320
+    d = workloads.decode_inputs(B, H, lens, S_max=S_max, seed=2007)
+    w_uv = workloads.w_uv_weights(H=H, seed=2008)
+    o, _, _ = decode(d, 4)
+    o_v = binding.mla_up_proj_v(o, w_uv.to(DEV))
+    sync()
+    ref = OM.mla_decode_values_explicit_ref(np64(d["q_lat"]), np64(d["q_rope"]), np64(w_uv), np64(d["cache"]),
+                                            lens, SCALE)
+    check_bf16(o_v, ref, "decode + W_UV vs explicit values")
+
+
 @pytest.mark.parametrize("S", [1, 2, 5, 32])
 def test_combine_standalone(S):
     B, H = 3, 20

@@ -166,3 +166,46 @@ def test_combine_closed_forms():
     w = np.exp([2.0, -1.0, 0.5])
     np.testing.assert_allclose(L2[0, 1], math.log(w.sum()), atol=1e-14)
     np.testing.assert_allclose(O2[0, 1], (w[:, None] * o[0, 1]).sum(0) / w.sum(), atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Value up-projection W_UV
+# ---------------------------------------------------------------------------
+def test_up_projection_equals_attention_over_decompressed_values():
+    # Attention is linear in its values: projecting the latent output equals
+    # attending over V_h = c W_UV[h].  The two sides share only the scores.
+    B, H, S_max, Dv = 2, 3, 40, 16
+    q_lat, q_rope, cache = make(B, H, S_max, 71)
+    w_uv = rnd((H, 512, Dv), 72, 0.05)
+    lens = np.array([40, 17])
+    scale = 1 / math.sqrt(576)
+    O, _ = M.mla_decode_ref(q_lat, q_rope, cache, lens, scale)
+    got = M.up_project_v_ref(O, w_uv)
+    ref = M.mla_decode_values_explicit_ref(q_lat, q_rope, w_uv, cache, lens, scale)
+    assert np.abs(got - ref).max() < 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_up_projection_selection_matrix_copies_dims():
+    # W_UV[h] = columns of the identity picking latent dims sel[h]: the
+    # projection returns exactly those dims of the latent output.
+    B, H, Dv = 3, 2, 8
+    o = rnd((B, H, 512), 73)
+    sel = [np.arange(Dv) * 7 + 3, np.arange(Dv)[::-1] * 5 + 100]
+    w = np.zeros((H, 512, Dv))
+    for h in range(H):
+        w[h, sel[h], np.arange(Dv)] = 1.0
+    got = M.up_project_v_ref(o, w)
+    for h in range(H):
+        assert np.array_equal(got[:, h, :], o[:, h, sel[h]])
+
+
+def test_up_projection_brute_force_tiny():
+    B, H, Dl, Dv = 2, 2, 6, 3
+    o = rnd((B, H, Dl), 74)
+    w = rnd((H, Dl, Dv), 75)
+    got = M.up_project_v_ref(o, w)
+    for b in range(B):
+        for h in range(H):
+            for d in range(Dv):
+                ref = math.fsum(float(o[b, h, c]) * float(w[h, c, d]) for c in range(Dl))
+                assert abs(got[b, h, d] - ref) < 1e-12
