@@ -73,6 +73,24 @@ mla_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       mla_dtype_t dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_chunk - attn_fwd for a chunk of Nq queries against Nk keys
+ * (prefill of a chunk over an existing cache).  The queries are the last Nq
+ * positions of the key sequence, so the causal mask ([FA2-v2 blog] section
+ * 3.4, generalised) is aligned at the bottom right: query row i sees keys
+ * 0 .. i + (Nk - Nq).  With Nq = Nk this is attn_fwd.  A row that sees no
+ * key (only when Nq > Nk) gets O = 0 and LSE = -inf.
+ *
+ * q, o : [B, H, Nq, D]     k, v : [B, H, Nk, D]     lse : [B, H, Nq] f32
+ * Other arguments, dtypes, sizes (Nq, Nk each 0 .. 2^20), alignment and
+ * errors as attn_fwd; Nq = 0 enqueues nothing, Nk = 0 gives every row
+ * O = 0 and LSE = -inf.  q and o may be NULL when Nq = 0, k and v when
+ * Nk = 0 (empty tensors); otherwise NULL gives MLA_ERR_NULL.
+ */
+mla_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                            mla_dtype_t dtype, hipStream_t stream);
+
+/*
  * mla_decode_workspace_size - bytes of device workspace mla_decode_fwd needs
  * for (B, H, num_splits) on the CURRENT device (the size depends on its
  * compute-unit count).  Returns 0 if the arguments are invalid or the device

@@ -10,6 +10,7 @@ missing.  There is no CPU fallback.
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_chunk",
     "mla_decode_fwd",
     "mla_decode_workspace_size",
     "mla_combine",

@@ -18,7 +18,7 @@ _lib = None
 MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(7)
 MLA_F32, MLA_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "mla_decode_workspace_size", "mla_decode_fwd", "mla_combine", "mla_absorb_q",
+EXPORTED = ("attn_fwd", "attn_fwd_chunk", "mla_decode_workspace_size", "mla_decode_fwd", "mla_combine", "mla_absorb_q",
             "mla_up_proj_v",
             "mla_status_string")
 
@@ -44,6 +44,8 @@ def load(path=None):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.attn_fwd.restype = i
+    lib.attn_fwd_chunk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_chunk.restype = i
     lib.mla_decode_workspace_size.argtypes = [i, i, i]
     lib.mla_decode_workspace_size.restype = sz
     lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, vp, sz, vp]
@@ -114,6 +116,31 @@ def attn_fwd(q, k, v, scale, causal, o=None, lse=None, want_lse=True):
     st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D, float(scale),
                          int(bool(causal)), dt, _stream(q.device))
     _check("attn_fwd", st)
+    return o, lse
+
+
+def attn_fwd_chunk(q, k, v, scale, causal, o=None, lse=None, want_lse=True):
+    """Attention of Nq queries against Nk keys, causal mask aligned bottom
+    right (row i sees keys <= i + Nk - Nq). q [B,H,Nq,D]; k, v [B,H,Nk,D].
+    Returns (o [B,H,Nq,D], lse [B,H,Nq] or None)."""
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    dt = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}.get(q.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _need(q, "q", q.dtype, (B, H, Nq, D))
+    _need(k, "k", q.dtype, (B, H, Nk, D))
+    _need(v, "v", q.dtype, (B, H, Nk, D))
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", q.dtype, (B, H, Nq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H, Nq))
+    st = load().attn_fwd_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, D, float(scale),
+                               int(bool(causal)), dt, _stream(q.device))
+    _check("attn_fwd_chunk", st)
     return o, lse
 
 

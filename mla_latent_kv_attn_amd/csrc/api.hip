@@ -16,9 +16,9 @@
 
 namespace mla {
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
-                               int N, float scale, bool causal, hipStream_t stream);
+                               int Nq, int Nk, float scale, bool causal, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse, int B,
-                                int H, int N, float scale, bool causal, hipStream_t stream);
+                                int H, int Nq, int Nk, float scale, bool causal, hipStream_t stream);
 hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __bf16* cache, const int* seqlens,
                              __bf16* o, float* lse, int B, int H, int S_max, float scale, int num_splits,
                              const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream);
@@ -94,10 +94,15 @@ MLA_EXPORT const char* mla_status_string(mla_status_t s) {
     return "unknown mla_status_t";
 }
 
-MLA_EXPORT mla_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                                 int N, int D, float scale, int causal, mla_dtype_t dtype, hipStream_t stream) {
-    if (!q || !k || !v || !o) return MLA_ERR_NULL;
-    if (B < 1 || H < 1 || N < 0 || D < 1 || N > (1 << 20) || (long long)B * H > INT_MAX) return MLA_ERR_SHAPE;
+namespace {
+// Shared by attn_fwd (Nq = Nk) and attn_fwd_chunk.
+mla_status_t attn_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                         int Nk, int D, float scale, int causal, mla_dtype_t dtype, hipStream_t stream) {
+    // Empty tensors may come as NULL: q, o are needed only for Nq > 0, k, v for Nk > 0.
+    if ((Nq != 0 && (!q || !o)) || (Nk != 0 && (!k || !v))) return MLA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 0 || Nk < 0 || D < 1 || Nq > (1 << 20) || Nk > (1 << 20) ||
+        (long long)B * H > INT_MAX)
+        return MLA_ERR_SHAPE;
     if ((causal != 0 && causal != 1) || !good_scale(scale)) return MLA_ERR_SHAPE;
     if (dtype == MLA_F32) {
         if (D != 64) return MLA_ERR_UNSUPPORTED;
@@ -108,17 +113,29 @@ MLA_EXPORT mla_status_t attn_fwd(const void* q, const void* k, const void* v, vo
     }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
         return MLA_ERR_ALIGN;
-    if (N == 0) return MLA_OK;
+    if (Nq == 0) return MLA_OK;
     hipError_t e;
     if (dtype == MLA_F32)
         e = mla::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                     static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, N, scale,
+                                     static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, Nq, Nk, scale,
                                      causal == 1, stream);
     else
         e = mla::launch_attn_fwd_bf16(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, H, N, scale,
+                                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, B, H, Nq, Nk, scale,
                                       causal == 1, stream);
     return hip_status(e);
+}
+}  // namespace
+
+MLA_EXPORT mla_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                 int N, int D, float scale, int causal, mla_dtype_t dtype, hipStream_t stream) {
+    return attn_common(q, k, v, o, lse, B, H, N, N, D, scale, causal, dtype, stream);
+}
+
+MLA_EXPORT mla_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                       int H, int Nq, int Nk, int D, float scale, int causal, mla_dtype_t dtype,
+                                       hipStream_t stream) {
+    return attn_common(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, stream);
 }
 
 MLA_EXPORT size_t mla_decode_workspace_size(int B, int H, int num_splits) {

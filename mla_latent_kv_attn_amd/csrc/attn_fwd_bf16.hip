@@ -73,7 +73,7 @@ __device__ __forceinline__ int b16_key_of_reg(int e, int g) {
 template <bool CAUSAL>
 __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, int num_q_tiles, float c_log2) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int BH, int num_q_tiles, float c_log2) {
     __shared__ __attribute__((aligned(1024))) char smem[2][2][B16_TILE_BYTES];  // [buf][K|V]
 
     // Work mapping: the id's low part is batch*head, so every (b,h) stays on
@@ -84,7 +84,10 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     const int rank = id / BH;
     const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
     const int q_start = qt * B16_BR;
-    const size_t base = (size_t)bh * N * B16_D;
+    const size_t base = (size_t)bh * Nq * B16_D;     // Q, O
+    const size_t kbase = (size_t)bh * Nk * B16_D;    // K, V
+    // Causal mask aligned at the bottom right: row i sees keys <= i + off.
+    const int off = Nk - Nq;
 
     const int w = wave_id();
     const int lane = lane_id();
@@ -95,14 +98,27 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     // Q as the B operand of S^T = K Q^T: lane holds row wrow0+n, dims 16kk+8g..+7.
     bf16x8 qf[B16_D / 16];
     {
-        const int r = min(wrow0 + n, N - 1);
+        const int r = min(wrow0 + n, Nq - 1);
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + base + (size_t)r * B16_D);
 #pragma unroll
         for (int kk = 0; kk < B16_D / 16; ++kk) qf[kk] = qp[2 * kk + g];
     }
 
-    const int kv_limit = CAUSAL ? min(q_start + B16_BR, N) : N;
+    const int kv_limit = max(CAUSAL ? min(q_start + B16_BR + off, Nk) : Nk, 0);
     const int Tc = (kv_limit + B16_BC - 1) / B16_BC;
+    if (Tc == 0) {  // no row of this tile sees a key (Nq > Nk): O = 0, LSE = -inf
+        const int row = wrow0 + n;
+        if (row < Nq) {
+            __bf16* op = o + base + (size_t)row * B16_D;
+            bf16x4 z;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = to_bf16(0.f);
+#pragma unroll
+            for (int c = 0; c < B16_D / 8; ++c) *reinterpret_cast<bf16x4*>(op + 8 * c + 4 * g) = z;
+            if (lse && g == 0) lse[(size_t)bh * Nq + row] = -INFINITY;
+        }
+        return;
+    }
 
     // Copy i (0..16) of 64 chunks of the K and of the V tile is issued by wave
     // i % 4.  Chunk L is row L / 17, chunk L % 17 (the pad chunk 16 repeats
@@ -119,9 +135,9 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     }
     auto issue_tile = [&](int j, int buf) {
         const int kv_start = j * B16_BC;
-        const uint32_t bytes = (uint32_t)(N - kv_start) * (uint32_t)(B16_D * 2);
-        const auto rk = make_rsrc(k + base + (size_t)kv_start * B16_D, bytes);
-        const auto rv = make_rsrc(v + base + (size_t)kv_start * B16_D, bytes);
+        const uint32_t bytes = (uint32_t)(Nk - kv_start) * (uint32_t)(B16_D * 2);
+        const auto rk = make_rsrc(k + kbase + (size_t)kv_start * B16_D, bytes);
+        const auto rv = make_rsrc(v + kbase + (size_t)kv_start * B16_D, bytes);
         static_for<B16_COPIES_HI>([&](auto kc_c) {
             constexpr int kc = decltype(kc_c)::value;
             if (kc < B16_COPIES_LO || w == 0) {
@@ -214,11 +230,11 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
             for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s0[e]);
 #pragma unroll
             for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s1[e]);
-            const bool tail = kv_start + B16_BC > N;
-            const bool diag = CAUSAL && (kv_start + B16_BC - 1 > wrow0);
+            const bool tail = kv_start + B16_BC > Nk;
+            const bool diag = CAUSAL && (kv_start + B16_BC - 1 > wrow0 + off);
             if (tail || diag) {
                 const int row = wrow0 + n;
-                const int lim = diag ? min(row + 1, N) : N;
+                const int lim = diag ? min(row + off + 1, Nk) : Nk;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = kv_start + b16_key_of_reg(e, g);
@@ -282,8 +298,9 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     // Epilogue: O = Oacc / l; O^T register e of block db: dim 32db + 8(e/4) + 4g + e%4.
     l = sum2_halves(l);
     const int row = wrow0 + n;
-    if (row < N) {
-        const float inv_l = 1.f / l;
+    if (row < Nq) {
+        // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
         __bf16* op = o + base + (size_t)row * B16_D;
 #pragma unroll
         for (int db = 0; db < B16_D / 32; ++db)
@@ -294,23 +311,23 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                 for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][4 * i + r] * inv_l);
                 *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i + 4 * g) = t;
             }
-        if (lse && g == 0) lse[(size_t)bh * N + row] = (m + __builtin_log2f(l)) * kLn2;
+        if (lse && g == 0) lse[(size_t)bh * Nq + row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
 hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,
-                                int B, int H, int N, float scale, bool causal, hipStream_t stream) {
+                                int B, int H, int Nq, int Nk, float scale, bool causal, hipStream_t stream) {
     const int BH = B * H;
-    const int nqt = (N + B16_BR - 1) / B16_BR;
+    const int nqt = (Nq + B16_BR - 1) / B16_BR;
     const long long grid = (long long)nqt * BH;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float c = scale * kLog2e;
     if (causal)
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)grid), dim3(B16_THREADS), 0, stream,
-                           q, k, v, o, lse, N, BH, nqt, c);
+                           q, k, v, o, lse, Nq, Nk, BH, nqt, c);
     else
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)grid), dim3(B16_THREADS), 0, stream,
-                           q, k, v, o, lse, N, BH, nqt, c);
+                           q, k, v, o, lse, Nq, Nk, BH, nqt, c);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ constexpr int F32_LOADS_PER_WAVE = (F32_BC * F32_D * 4) / (16 * 64) / (F32_THREA
 template <bool CAUSAL>
 __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int N, int BH, int num_q_tiles, float scale_log2) {
+    float* __restrict__ o, float* __restrict__ lse, int Nq, int Nk, int BH, int num_q_tiles, float scale_log2) {
     __shared__ __attribute__((aligned(16))) float Ks[2][F32_BC * F32_D];
     __shared__ __attribute__((aligned(16))) float Vs[2][F32_BC * F32_D];
 
@@ -46,14 +46,17 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
     const int rank = id / BH;
     const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
     const int q_start = qt * F32_BR;
-    const size_t base = (size_t)bh * N * F32_D;
+    const size_t base = (size_t)bh * Nq * F32_D;     // Q, O
+    const size_t kbase = (size_t)bh * Nk * F32_D;    // K, V
+    // Causal mask aligned at the bottom right: row i sees keys <= i + off.
+    const int off = Nk - Nq;
 
     const int tid = threadIdx.x;
     const int w = wave_id();
     const int lane = lane_id();
     const int row = q_start + tid;
-    const bool row_valid = row < N;
-    const int row_c = row_valid ? row : (N - 1);
+    const bool row_valid = row < Nq;
+    const int row_c = row_valid ? row : (Nq - 1);
 
     // Query row into registers, pre-scaled into the log2 domain.
     float qr[F32_D];
@@ -69,8 +72,8 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
         }
     }
 
-    const int kv_limit = CAUSAL ? min(q_start + F32_BR, N) : N;
-    const int Tc = (kv_limit + F32_BC - 1) / F32_BC;
+    const int kv_limit = max(CAUSAL ? min(q_start + F32_BR + off, Nk) : Nk, 0);
+    const int Tc = (kv_limit + F32_BC - 1) / F32_BC;  // 0 when no row of the tile sees a key
 
     // Tile loader: wave w copies chunks [w*L*64, (w+1)*L*64) of 16 bytes of
     // the K tile and of the V tile (L = loads per wave per tile).
@@ -82,8 +85,8 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
             const int chunk = chunk0 + lane;
             const int r = chunk / (F32_D / 4);
             const int c4 = chunk % (F32_D / 4);
-            const int key = min(kv_start + r, N - 1);
-            const size_t goff = base + (size_t)key * F32_D + c4 * 4;
+            const int key = min(kv_start + r, Nk - 1);
+            const size_t goff = kbase + (size_t)key * F32_D + c4 * 4;
             gload_lds16(k + goff, &Ks[buf][chunk0 * 4]);
             gload_lds16(v + goff, &Vs[buf][chunk0 * 4]);
         }
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
     for (int d = 0; d < F32_D; ++d) oacc[d] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    issue_tile(0, 0);
+    if (Tc > 0) issue_tile(0, 0);
     for (int j = 0; j < Tc; ++j) {
         const int buf = j & 1;
         if (j + 1 < Tc) {
@@ -125,10 +128,10 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
         }
         // Masks: keys past N only on the last tile; causal element mask only
         // on tiles that straddle the diagonal (section 3.4).
-        const bool tail = kv_start + F32_BC > N;
-        const bool diag = CAUSAL && (kv_start + F32_BC - 1 > q_start);
+        const bool tail = kv_start + F32_BC > Nk;
+        const bool diag = CAUSAL && (kv_start + F32_BC - 1 > q_start + off);
         if (tail || diag) {
-            const int lim = diag ? min(row_c + 1, N) : N;
+            const int lim = diag ? min(row_c + off + 1, Nk) : Nk;
 #pragma unroll
             for (int c = 0; c < F32_BC; ++c)
                 if (kv_start + c >= lim) s[c] = -INFINITY;
@@ -165,30 +168,31 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
     }
 
     if (row_valid) {
-        const float inv_l = 1.f / l;
+        // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
         float4* op = reinterpret_cast<float4*>(o + base + (size_t)row * F32_D);
 #pragma unroll
         for (int i = 0; i < F32_D / 4; ++i)
             op[i] = make_float4(oacc[4 * i] * inv_l, oacc[4 * i + 1] * inv_l, oacc[4 * i + 2] * inv_l,
                                 oacc[4 * i + 3] * inv_l);
-        if (lse) lse[(size_t)bh * N + row] = (m + __builtin_log2f(l)) * kLn2;
+        if (lse) lse[(size_t)bh * Nq + row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
 // Host-side launcher (called by the C ABI after validation).
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                               int B, int H, int N, float scale, bool causal, hipStream_t stream) {
+                               int B, int H, int Nq, int Nk, float scale, bool causal, hipStream_t stream) {
     const int BH = B * H;
-    const int nqt = (N + F32_BR - 1) / F32_BR;
+    const int nqt = (Nq + F32_BR - 1) / F32_BR;
     const long long grid = (long long)nqt * BH;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float sl2 = scale * kLog2e;
     if (causal)
         hipLaunchKernelGGL(attn_fwd_f32_kernel<true>, dim3((unsigned)grid), dim3(F32_THREADS), 0, stream,
-                           q, k, v, o, lse, N, BH, nqt, sl2);
+                           q, k, v, o, lse, Nq, Nk, BH, nqt, sl2);
     else
         hipLaunchKernelGGL(attn_fwd_f32_kernel<false>, dim3((unsigned)grid), dim3(F32_THREADS), 0, stream,
-                           q, k, v, o, lse, N, BH, nqt, sl2);
+                           q, k, v, o, lse, Nq, Nk, BH, nqt, sl2);
     return hipGetLastError();
 }
 

@@ -24,7 +24,11 @@ Pinned by (tests/test_oracle_attention.py): pure-Python brute force on tiny
 inputs, torch's fp64 CPU scaled_dot_product_attention, row sums of P = 1,
 causal row 0 = V[0], identical keys -> mean of V (closed form, also per causal
 prefix), two-key sigmoid closed form, joint permutation invariance of (K, V),
-and the blog's printed worked example and launch arithmetic.
+and the blog's printed worked example and launch arithmetic.  The
+non-square causal form (Nq != Nk) is pinned by chunk consistency (the last
+Nq rows of a square causal attention, run as a chunk against all keys),
+Nq = 1 (sees every key), rows with no key (Nq > Nk), pure-Python loops, and
+torch's fp64 SDPA with an explicit boolean mask.
 """
 
 import numpy as np
@@ -47,23 +51,26 @@ def _f64(x):
 def attn_ref(q, k, v, scale, causal, row_block=256):
     """Explicit softmax attention and per-row LSE.
 
-    q, k: [B, H, N, D]; v: [B, H, N, Dv] (any real dtype, upcast to float64).
-    Returns (O [B, H, N, Dv] float64, LSE [B, H, N] float64).
+    q: [B, H, Nq, D]; k: [B, H, Nk, D]; v: [B, H, Nk, Dv] (any real dtype,
+    upcast to float64).  Returns (O [B, H, Nq, Dv] float64, LSE [B, H, Nq]).
 
     Rows are processed in blocks of ``row_block`` only to bound memory; each
     block's softmax is over the full key range, so blocking changes nothing.
     Definition: [FA2-v2 blog] section 1.3 (O = softmax(S) V, deferred
     normalisation being an exact rewrite of it) and section 3.4 (causal:
-    row i sees keys 0..i).
+    row i sees keys 0..i).  With Nq != Nk the causal mask is aligned at the
+    bottom right (the queries are the last Nq positions of the key sequence,
+    as in a prefill chunk over an existing cache): row i sees keys
+    0..i + (Nk - Nq).  A row that sees no key (Nq > Nk) gives O = 0 and
+    LSE = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, _ = q.shape
     Nk = k.shape[2]
     Dv = v.shape[3]
-    if causal and Nk != N:
-        raise ValueError("causal attention here is square (N_q == N_k)")
+    off = Nk - N
     O = np.zeros((B, H, N, Dv))
-    LSE = np.zeros((B, H, N))
+    LSE = np.full((B, H, N), -np.inf)
     keys = np.arange(Nk)
     for b in range(B):
         for h in range(H):
@@ -72,12 +79,17 @@ def attn_ref(q, k, v, scale, causal, row_block=256):
                 S = scale * (q[b, h, r0:r1] @ k[b, h].T)
                 if causal:
                     rows = np.arange(r0, r1)[:, None]
-                    S = np.where(keys[None, :] > rows, -np.inf, S)
-                m = S.max(axis=1, keepdims=True)
-                E = np.exp(S - m)
+                    S = np.where(keys[None, :] > rows + off, -np.inf, S)
+                seen = np.isfinite(S).any(axis=1)
+                if not seen.any():
+                    continue
+                Ss = S[seen]
+                m = Ss.max(axis=1, keepdims=True)
+                E = np.exp(Ss - m)
                 l = E.sum(axis=1, keepdims=True)
-                O[b, h, r0:r1] = (E / l) @ v[b, h]
-                LSE[b, h, r0:r1] = (m + np.log(l))[:, 0]
+                idx = np.arange(r0, r1)[seen]
+                O[b, h, idx] = (E / l) @ v[b, h]
+                LSE[b, h, idx] = (m + np.log(l))[:, 0]
     return O, LSE
 
 

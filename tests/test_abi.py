@@ -68,6 +68,21 @@ def test_attn_validation_codes(lib):
     assert _attn(lib, N=0) == binding.MLA_OK        # nothing to do, nothing enqueued
 
 
+def _chunk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=64, Nk=256, D=64, scale=0.125, causal=1, dt=0):
+    return lib.attn_fwd_chunk(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dt, None)
+
+
+def test_attn_chunk_validation_codes(lib):
+    assert _chunk(lib, v=None) == binding.MLA_ERR_NULL
+    assert _chunk(lib, Nq=-1) == binding.MLA_ERR_SHAPE
+    assert _chunk(lib, Nk=-1) == binding.MLA_ERR_SHAPE
+    assert _chunk(lib, Nk=(1 << 20) + 1) == binding.MLA_ERR_SHAPE
+    assert _chunk(lib, causal=3) == binding.MLA_ERR_SHAPE
+    assert _chunk(lib, D=128, dt=0) == binding.MLA_ERR_UNSUPPORTED
+    assert _chunk(lib, o=BAD) == binding.MLA_ERR_ALIGN
+    assert _chunk(lib, Nq=0) == binding.MLA_OK      # nothing to do, nothing enqueued
+
+
 def _dec(lib, ql=P, qr=P, c=P, sl=P, o=P, lse=P, B=2, H=128, S=64, scale=0.04, ns=4, ws=P, wsb=1 << 30):
     return lib.mla_decode_fwd(ql, qr, c, sl, o, lse, B, H, S, scale, ns, ws, wsb, None)
 

@@ -130,3 +130,38 @@ def test_lse_optional_and_outputs_untouched_on_error():
         binding.attn_fwd(q, k, v, -1.0, False, o=canary)
     sync()
     assert torch.all(canary == 7.0)
+
+
+# ------------------------------------------------- chunk (Nq != Nk) ----
+CHUNKS = [(64, 256), (33, 300), (200, 1000), (128, 128), (300, 100), (1, 513), (5, 0)]
+
+
+def chunk_inputs(B, H, Nq, Nk, D, dtype, seed):
+    q = workloads.attn_inputs(B, H, Nq, D, dtype, seed=seed)[0]
+    _, k, v = workloads.attn_inputs(B, H, Nk, D, dtype, seed=seed + 1)
+    return q, k, v
+
+
+@pytest.mark.parametrize("Nq,Nk", CHUNKS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_chunk(Nq, Nk, causal):
+    say(f"fp32 chunk Nq={Nq} Nk={Nk} causal={causal}")
+    q, k, v = chunk_inputs(2, 3, Nq, Nk, 64, torch.float32, 1300 + Nq + Nk)
+    o, l = binding.attn_fwd_chunk(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, causal)
+    sync()
+    Or, Lr = OA.attn_ref(np64(q), np64(k), np64(v), 0.125, causal)
+    check_f32(o, Or, "O")
+    check_lse(l, Lr, "LSE")
+
+
+@pytest.mark.parametrize("Nq,Nk", CHUNKS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_chunk(Nq, Nk, causal):
+    say(f"bf16 chunk Nq={Nq} Nk={Nk} causal={causal}")
+    q, k, v = chunk_inputs(1, 3, Nq, Nk, 128, torch.bfloat16, 1700 + Nq + Nk)
+    sc = 1 / math.sqrt(128)
+    o, l = binding.attn_fwd_chunk(q.to(DEV), k.to(DEV), v.to(DEV), sc, causal)
+    sync()
+    Or, Lr = OA.attn_ref(np64(q), np64(k), np64(v), sc, causal)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")

@@ -175,3 +175,74 @@ def test_blog_launch_and_shared_memory_arithmetic():
     assert round(total / 1024) == g["shared_total_KiB"]
     assert total == g["shared_total_bytes"]
     assert int(qo / 1000) == g["qs_oacc_kB"]
+
+
+# ---------------------------------------------------------------------------
+# Non-square causal attention (a prefill chunk of Nq queries over Nk keys)
+# ---------------------------------------------------------------------------
+def brute_force_chunk(q, k, v, scale):
+    """Scalar loops, bottom-right causal: row i sees keys j <= i + Nk - Nq."""
+    N, Nk, D, Dv = len(q), len(k), len(q[0]), len(v[0])
+    off = Nk - N
+    O, LSE = [], []
+    for i in range(N):
+        s = [(j, scale * math.fsum(float(q[i][d]) * float(k[j][d]) for d in range(D)))
+             for j in range(Nk) if j <= i + off]
+        if not s:
+            O.append([0.0] * Dv)
+            LSE.append(-math.inf)
+            continue
+        mx = max(x for _, x in s)
+        w = [(j, math.exp(x - mx)) for j, x in s]
+        tot = math.fsum(x for _, x in w)
+        O.append([math.fsum(x * float(v[j][c]) for j, x in w) / tot for c in range(Dv)])
+        LSE.append(mx + math.log(tot))
+    return np.array(O), np.array(LSE)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(3, 7), (5, 5), (7, 3), (1, 6), (6, 1)])
+def test_chunk_brute_force(Nq, Nk):
+    D, Dv = 4, 3
+    q, k, v = rnd((1, 1, Nq, D), 11), rnd((1, 1, Nk, D), 12), rnd((1, 1, Nk, Dv), 13)
+    O, L = A.attn_ref(q, k, v, 0.41, True)
+    Ob, Lb = brute_force_chunk(q[0, 0], k[0, 0], v[0, 0], 0.41)
+    np.testing.assert_allclose(O[0, 0], Ob, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(L[0, 0]), np.isneginf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[0, 0][fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+def test_chunk_equals_last_rows_of_square_causal():
+    # The queries of a chunk are the last Nq positions of the key sequence:
+    # their rows of a full square causal attention are the chunk's result.
+    B, H, Nk, D = 2, 2, 50, 8
+    q, k, v = rnd((B, H, Nk, D), 14), rnd((B, H, Nk, D), 15), rnd((B, H, Nk, D), 16)
+    O, L = A.attn_ref(q, k, v, 0.3, True)
+    for Nq in (1, 17, 50):
+        Oc, Lc = A.attn_ref(q[:, :, Nk - Nq:], k, v, 0.3, True, row_block=7)
+        np.testing.assert_allclose(Oc, O[:, :, Nk - Nq:], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(Lc, L[:, :, Nk - Nq:], rtol=0, atol=1e-12)
+
+
+def test_chunk_single_query_sees_every_key_and_empty_rows():
+    q, k, v = rnd((1, 2, 1, 8), 17), rnd((1, 2, 30, 8), 18), rnd((1, 2, 30, 5), 19)
+    O, L = A.attn_ref(q, k, v, 0.5, True)
+    On, Ln = A.attn_ref(q, k, v, 0.5, False)
+    np.testing.assert_allclose(O, On, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L, Ln, rtol=0, atol=1e-13)
+    # Nq > Nk: the first Nq - Nk rows see no key
+    q2 = rnd((1, 1, 9, 8), 20)
+    O2, L2 = A.attn_ref(q2, k[:, :1, :4], v[:, :1, :4], 0.5, True)
+    assert np.all(O2[0, 0, :5] == 0) and np.all(np.isneginf(L2[0, 0, :5]))
+    assert np.all(np.isfinite(L2[0, 0, 5:]))
+
+
+def test_chunk_against_torch_sdpa_with_explicit_mask():
+    B, H, Nq, Nk, D = 2, 3, 21, 45, 16
+    q, k, v = rnd((B, H, Nq, D), 21), rnd((B, H, Nk, D), 22), rnd((B, H, Nk, D), 23)
+    scale = 1 / math.sqrt(D)
+    O, _ = A.attn_ref(q, k, v, scale, True, row_block=8)
+    allowed = torch.from_numpy(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq))
+    Ot = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=allowed, scale=scale).numpy()
+    np.testing.assert_allclose(O, Ot, rtol=0, atol=1e-12)
