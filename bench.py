@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
-    ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32", "copy"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32", "prefill_chunk", "copy"],
+                    default=None,
                     help="run only one workload (for profiling); 'copy' is a plain 256 MiB device copy "
                          "used to calibrate the HBM byte counters")
     return ap.parse_args()
@@ -167,6 +168,38 @@ def bench_prefill(log, name, causal, reps=None):
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
 
 
+def chunk_pairs(Nq, Nk, causal):
+    """Visible (query, key) pairs of one (b, h) for a chunk: row i sees keys
+    0..i + Nk - Nq when causal, all Nk otherwise."""
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    return sum(max(0, min(i + off + 1, Nk)) for i in range(Nq))
+
+
+def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007):
+    """bf16 prefill of a chunk of Nq new queries over Nk keys (causal, bottom-right)."""
+    import torch
+    from mla_latent_kv_attn_amd import binding, workloads
+    dev = "cuda:0"
+    q = workloads.attn_inputs(B, H, Nq, D, torch.bfloat16, seed=seed)[0].to(dev)
+    _, k, v = workloads.attn_inputs(B, H, Nk, D, torch.bfloat16, seed=seed + 1)
+    k, v = k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    fn = lambda: binding.attn_fwd_chunk(q, k, v, 1.0 / math.sqrt(D), True, o=o, lse=lse)
+    for _ in range(20):
+        fn()
+    torch.cuda.synchronize()
+    ms = time_events(fn, 50)
+    avg = sum(ms) / len(ms)
+    tf = 4.0 * D * B * H * chunk_pairs(Nq, Nk, True) / (avg * 1e-3) / 1e12
+    log(f"prefill chunk bf16 Nq={Nq} Nk={Nk}: {avg:.3f} ms, {tf:.1f} TFLOP/s ({100*tf/BF16_PEAK_TFLOPS:.1f}%)")
+    return {"workload": f"attn_fwd_chunk bf16 B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal=1 (bottom-right)",
+            "ms": round(avg, 4), "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma"}
+
+
 DECODE_SOURCES = ("mla_latent_kv_attn_amd/csrc/mla_decode.hip", "mla_latent_kv_attn_amd/csrc/mla_plan.h",
                   "mla_latent_kv_attn_amd/csrc/common.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_varlen_pmc.json")
@@ -256,6 +289,9 @@ def main():
     if args.only == "prefill_bf16":
         bench_prefill(log, "attn_bf16", True, reps=args.steps)
         return
+    if args.only == "prefill_chunk":
+        bench_prefill_chunk(log)
+        return
     if args.only == "prefill_fp32":
         bench_prefill(log, "attn_fp32", False, reps=args.steps)
         return
@@ -267,6 +303,7 @@ def main():
         prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True)
         prefill["fp32_noncausal"] = bench_prefill(log, "attn_fp32", False, reps=5)
         prefill["fp32_causal"] = bench_prefill(log, "attn_fp32", True, reps=5)
+        prefill["bf16_chunk"] = bench_prefill_chunk(log)
     cpu = None if args.no_cpu else cpu_baseline(d, log)
     value = d["kv_bytes"] / (d["ms_step"] * 1e-3) / 1e9
     achieved = d["kv_bytes"] / (d["dec_ms"] * 1e-3) / 1e9
