@@ -8,7 +8,9 @@
 //
 // Tiling (D = 128): a workgroup owns Br = 128 query rows of one (b, h);
 // wave w owns rows 32w..32w+31.  Key/value tiles of Bc = 64 rows are copied
-// global -> LDS (buffer_load_dwordx4 ... lds) into a double buffer.  Each
+// global -> LDS (buffer_load_dwordx4 ... lds) into a double buffer, with the
+// 16-byte chunks of each row permuted so that every LDS read is free of
+// bank conflicts.  Each
 // wave's per-lane source offsets within a tile are fixed; a tile only moves
 // the buffer base, and the buffer ends at key N - 1, so keys past N read as
 // zeros (and are masked).  LDS fragments are read with inline asm and waited
@@ -39,15 +41,12 @@ constexpr int B16_BC = 64;
 constexpr int B16_WAVES = 4;
 constexpr int B16_THREADS = 64 * B16_WAVES;
 constexpr int B16_ROW_CHUNKS = B16_D * 2 / 16;                       // 16 chunks of 16 B per row
-constexpr int B16_STRIDE = (B16_ROW_CHUNKS + 1) * 16;                // 272 B per LDS row (== 16 mod 128)
-constexpr int B16_TILE_BYTES = B16_BC * B16_STRIDE;                  // 17408
-constexpr int B16_TILE_INSTR = B16_BC * (B16_ROW_CHUNKS + 1) / 64;   // 17 wave-wide 1 KiB copies per tile
-static_assert(B16_BC * (B16_ROW_CHUNKS + 1) % 64 == 0, "whole copies");
-static_assert(B16_TILE_INSTR % B16_WAVES == 1, "wave 0 issues the one extra copy");
-constexpr int B16_COPIES_HI = (B16_TILE_INSTR + B16_WAVES - 1) / B16_WAVES;  // copies per tile, wave 0
-constexpr int B16_COPIES_LO = B16_TILE_INSTR / B16_WAVES;                      // other waves
-constexpr int B16_LOADS_HI = 2 * B16_COPIES_HI;  // K + V copies, wave 0
-constexpr int B16_LOADS_LO = 2 * B16_COPIES_LO;  // other waves
+constexpr int B16_STRIDE = B16_ROW_CHUNKS * 16;                      // 256 B per LDS row, chunks swizzled
+constexpr int B16_TILE_BYTES = B16_BC * B16_STRIDE;                  // 16384
+constexpr int B16_TILE_INSTR = B16_BC * B16_ROW_CHUNKS / 64;         // 16 wave-wide 1 KiB copies per tile
+static_assert(B16_TILE_INSTR % B16_WAVES == 0, "copies split evenly over the waves");
+constexpr int B16_COPIES = B16_TILE_INSTR / B16_WAVES;  // copies per tile and wave, K and V each
+constexpr int B16_LOADS = 2 * B16_COPIES;               // K + V copies per tile and wave
 // LDS fragment prefetch distances (MFMA steps) of the score and PV loops.
 #ifndef MLA_B16_PF
 #define MLA_B16_PF 2
@@ -58,17 +57,25 @@ constexpr int B16_LOADS_LO = 2 * B16_COPIES_LO;  // other waves
 constexpr int B16_PF = MLA_B16_PF;
 constexpr int B16_PFV = MLA_B16_PFV;
 
-// LDS rows have a stride of 16 (mod 128) bytes.  Inside each 32-key block
-// MFMA row rho = 16a + 8b + 4g + c is fed key 16a + 8b + g + 2c, so that
-// (i) the eight rows one 8-lane group reads for S^T = K Q^T fall on eight
-// distinct 16-byte bank groups, (ii) register e of lane group g of S^T
-// holds key 16(e/8) + 8((e/4)%2) + g + 2(e%4), i.e. the eight registers of
-// k-step e/8 are P^T with logical k index 8g + e%8, and (iii) the four rows
-// each transposed V read touches are two apart, on distinct 32-byte groups.
+// Inside each 32-key block MFMA row rho = 16a + 8b + 4g + c is fed key
+// 16a + 8b + g + 2c, so that register e of lane group g of S^T holds key
+// 16(e/8) + 8((e/4)%2) + g + 2(e%4), i.e. the eight registers of k-step e/8
+// are P^T with logical k index 8g + e%8 (no data movement between the two
+// products).
 __device__ __forceinline__ int b16_kappa32(int rho) { return (rho & ~7) + ((rho >> 2) & 1) + 2 * (rho & 3); }
 __device__ __forceinline__ int b16_key_of_reg(int e, int g) {
     return 16 * (e >> 3) + 8 * ((e >> 2) & 1) + g + 2 * (e & 3);
 }
+// LDS tiles have 256-byte rows; 16-byte chunk c of row r is stored at chunk
+// position c ^ swz(r).  With 64 four-byte banks, ds_read_b128 serves 16 lanes
+// and ds_read_b64_tr_b16 32 lanes per pass.  The K swizzle puts the 16 rows
+// one 16-lane group reads on 16 distinct chunk positions; the V swizzle moves
+// rows 2jj, 2jj + 1 by 64 jj bytes, so the 32 lanes of one pass of a
+// transposed read (rows 2jj + {0,1}, one 64-byte column group) hit 64
+// distinct banks.  Both depend on r mod 16, so row offsets that are
+// multiples of 16 (and 8, for V) stay immediates.
+__device__ __forceinline__ int b16_kswz(int r) { return r & 15; }
+__device__ __forceinline__ int b16_vswz(int r) { return 4 * ((r >> 1) & 3); }
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
@@ -120,30 +127,27 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         return;
     }
 
-    // Copy i (0..16) of 64 chunks of the K and of the V tile is issued by wave
-    // i % 4.  Chunk L is row L / 17, chunk L % 17 (the pad chunk 16 repeats
-    // chunk 0).  Copy k of this wave has the fixed per-lane source offset
-    // voff[k] within a tile.
-    uint32_t voff[B16_COPIES_HI];
+    // Copy i (0..15) of 64 chunks of the K and of the V tile is issued by wave
+    // i % 4.  LDS chunk position L is row L / 16, position L % 16, which holds
+    // source chunk (L % 16) ^ swz(row); copy kc of this wave has the fixed
+    // per-lane source offsets koff[kc] (K) and voff[kc] (V) within a tile.
+    uint32_t koff[B16_COPIES], voff[B16_COPIES];
 #pragma unroll
-    for (int kc = 0; kc < B16_COPIES_HI; ++kc) {
-        const int L = (w + B16_WAVES * kc) * 64 + lane;
-        const int r = L / (B16_ROW_CHUNKS + 1);
-        int c = L - r * (B16_ROW_CHUNKS + 1);
-        c = (c == B16_ROW_CHUNKS) ? 0 : c;
-        voff[kc] = (uint32_t)(r * B16_D * 2 + 16 * c);
+    for (int kc = 0; kc < B16_COPIES; ++kc) {
+        const int L = (w + B16_WAVES * kc) * 64 + lane;  // LDS chunk position of this lane
+        const int r = L / B16_ROW_CHUNKS, p = L % B16_ROW_CHUNKS;
+        koff[kc] = (uint32_t)(r * B16_D * 2 + 16 * (p ^ b16_kswz(r)));
+        voff[kc] = (uint32_t)(r * B16_D * 2 + 16 * (p ^ b16_vswz(r)));
     }
     auto issue_tile = [&](int j, int buf) {
         const int kv_start = j * B16_BC;
         const uint32_t bytes = (uint32_t)(Nk - kv_start) * (uint32_t)(B16_D * 2);
         const auto rk = make_rsrc(k + kbase + (size_t)kv_start * B16_D, bytes);
         const auto rv = make_rsrc(v + kbase + (size_t)kv_start * B16_D, bytes);
-        static_for<B16_COPIES_HI>([&](auto kc_c) {
+        static_for<B16_COPIES>([&](auto kc_c) {
             constexpr int kc = decltype(kc_c)::value;
-            if (kc < B16_COPIES_LO || w == 0) {
-                bload_lds16(rk, &smem[buf][0][(w + B16_WAVES * kc) * 1024], voff[kc]);
-                bload_lds16(rv, &smem[buf][1][(w + B16_WAVES * kc) * 1024], voff[kc]);
-            }
+            bload_lds16(rk, &smem[buf][0][(w + B16_WAVES * kc) * 1024], koff[kc]);
+            bload_lds16(rv, &smem[buf][1][(w + B16_WAVES * kc) * 1024], voff[kc]);
         });
     };
 
@@ -156,12 +160,21 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     float l = 0.f;        // this lane's share of the running sum
 
     // Per-lane LDS byte offsets (all other offsets are immediates).
-    const uint32_t k_off = b16_kappa32(n) * B16_STRIDE + 16 * g;
+    // K: row kappa(n), chunk 2kk + g (one base per score k-step kk).
+    // V: row (G >> 1) + 2jj, chunk 4db + 2(G & 1) + qd / 2 (one base per dim block db).
+    constexpr int KS = B16_D / 16;  // score k-steps
     const int G = lane >> 4, sl = lane & 15;  // ds_read_b64_tr_b16 source lane = 4*jj + qd
     const int jj = sl >> 2, qd = sl & 3;
-    const uint32_t v_off = ((G >> 1) + 2 * jj) * B16_STRIDE + 32 * (G & 1) + 8 * qd;
+    uint32_t k_off[KS], v_off[4];
+    {
+        const int kr = b16_kappa32(n), vr = (G >> 1) + 2 * jj;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) k_off[kk] = kr * B16_STRIDE + 16 * ((2 * kk + g) ^ b16_kswz(kr));
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            v_off[db] = vr * B16_STRIDE + 16 * ((4 * db + 2 * (G & 1) + (qd >> 1)) ^ b16_vswz(vr)) + 8 * (qd & 1);
+    }
     const uint32_t smem_a = lds_addr(&smem[0][0][0]);
-    constexpr int KS = B16_D / 16;  // score k-steps
     constexpr int PS = 16;          // PV steps: (ks, db) = (step / 4, step % 4)
 
     issue_tile(0, 0);
@@ -169,13 +182,12 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     // loop body needs no wait on them (which would also stall on the next
     // tile's copies).  One uniform count, so the compiler sees the wait on
     // every path (wave 0 also waits for two of its tile-0 copies).
-    wait_vmcnt<B16_LOADS_LO>();
+    wait_vmcnt<B16_LOADS>();
     for (int j = 0; j < Tc; ++j) {
         const int buf = j & 1;
         if (j + 1 < Tc) {
             issue_tile(j + 1, buf ^ 1);
-            if (w == 0) wait_vmcnt<B16_LOADS_HI>();
-            else wait_vmcnt<B16_LOADS_LO>();
+            wait_vmcnt<B16_LOADS>();
         } else {
             wait_vmcnt<0>();
         }
@@ -187,14 +199,14 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         // control flow keeps the accumulators in place (a per-wave skip here
         // makes the compiler copy them on every tile).
         {
-            const uint32_t Kt = smem_a + buf * 2 * B16_TILE_BYTES + k_off;
-            const uint32_t Vt = smem_a + (buf * 2 + 1) * B16_TILE_BYTES + v_off;
+            const uint32_t Kt = smem_a + buf * 2 * B16_TILE_BYTES;
+            const uint32_t Vt = smem_a + (buf * 2 + 1) * B16_TILE_BYTES;
             // Score fragments: ring of B16_PF + 1 pairs (keys 0..31 and 32..63).
             bf16x8 fa[B16_PF + 1], fb[B16_PF + 1];
             auto rd_k = [&](auto kk_c) {
                 constexpr int kk = decltype(kk_c)::value;
-                fa[kk % (B16_PF + 1)] = ds_read16<32 * kk>(Kt);
-                fb[kk % (B16_PF + 1)] = ds_read16<32 * B16_STRIDE + 32 * kk>(Kt);
+                fa[kk % (B16_PF + 1)] = ds_read16<0>(Kt + k_off[kk]);
+                fb[kk % (B16_PF + 1)] = ds_read16<32 * B16_STRIDE>(Kt + k_off[kk]);
             };
             f32x16 s0, s1;
 #pragma unroll
@@ -216,8 +228,8 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
             auto rd_v = [&](auto st_c) {
                 constexpr int st = decltype(st_c)::value;
                 constexpr int ks = st / 4, db = st % 4;
-                fv[st % (B16_PFV + 1)] = join(ds_read_tr16<16 * ks * B16_STRIDE + 64 * db>(Vt),
-                                              ds_read_tr16<(16 * ks + 8) * B16_STRIDE + 64 * db>(Vt));
+                fv[st % (B16_PFV + 1)] = join(ds_read_tr16<16 * ks * B16_STRIDE>(Vt + v_off[db]),
+                                              ds_read_tr16<(16 * ks + 8) * B16_STRIDE>(Vt + v_off[db]));
             };
             static_for<B16_PFV>([&](auto i) { rd_v(i); });
             // Tile max on the raw MFMA results (in the same block as the MFMAs,
