@@ -139,16 +139,21 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         koff[kc] = (uint32_t)(r * B16_D * 2 + 16 * (p ^ b16_kswz(r)));
         voff[kc] = (uint32_t)(r * B16_D * 2 + 16 * (p ^ b16_vswz(r)));
     }
-    auto issue_tile = [&](int j, int buf) {
-        const int kv_start = j * B16_BC;
-        const uint32_t bytes = (uint32_t)(Nk - kv_start) * (uint32_t)(B16_D * 2);
-        const auto rk = make_rsrc(k + kbase + (size_t)kv_start * B16_D, bytes);
-        const auto rv = make_rsrc(v + kbase + (size_t)kv_start * B16_D, bytes);
-        static_for<B16_COPIES>([&](auto kc_c) {
-            constexpr int kc = decltype(kc_c)::value;
-            bload_lds16(rk, &smem[buf][0][(w + B16_WAVES * kc) * 1024], koff[kc]);
-            bload_lds16(rv, &smem[buf][1][(w + B16_WAVES * kc) * 1024], voff[kc]);
-        });
+    // Buffers of tile j's K and V rows.  A tile past the last one gets empty
+    // buffers: its copies write zeros into the free LDS slot and need no
+    // branch.
+    auto tile_rsrc = [&](int j, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
+        const int kv_start = j < Tc ? j * B16_BC : 0;
+        const uint32_t bytes = j < Tc ? (uint32_t)(Nk - kv_start) * (uint32_t)(B16_D * 2) : 0u;
+        rk = make_rsrc(k + kbase + (size_t)kv_start * B16_D, bytes);
+        rv = make_rsrc(v + kbase + (size_t)kv_start * B16_D, bytes);
+    };
+    // Copy c (0..B16_LOADS-1) of this wave for one tile: even c copy K chunk
+    // block c/2, odd c the V block.
+    auto issue_copy = [&](auto c_c, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int buf) {
+        constexpr int c = decltype(c_c)::value, kc = c / 2;
+        if constexpr (c % 2 == 0) bload_lds16(rk, &smem[buf][0][(w + B16_WAVES * kc) * 1024], koff[kc]);
+        else bload_lds16(rv, &smem[buf][1][(w + B16_WAVES * kc) * 1024], voff[kc]);
     };
 
     f32x16 oacc[B16_D / 32];
@@ -177,21 +182,21 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     const uint32_t smem_a = lds_addr(&smem[0][0][0]);
     constexpr int PS = 16;          // PV steps: (ks, db) = (step / 4, step % 4)
 
-    issue_tile(0, 0);
-    // The Q loads are older than tile 0's copies: wait for them here, so the
-    // loop body needs no wait on them (which would also stall on the next
-    // tile's copies).  One uniform count, so the compiler sees the wait on
-    // every path (wave 0 also waits for two of its tile-0 copies).
-    wait_vmcnt<B16_LOADS>();
+    {
+        __amdgpu_buffer_rsrc_t rk, rv;
+        tile_rsrc(0, rk, rv);
+        static_for<B16_LOADS>([&](auto c) { issue_copy(c, rk, rv, 0); });
+    }
+    // Tile j + 1 is copied during the score products of tile j, one copy per
+    // k-step, into the buffer that tile j - 1 used (free since the barrier
+    // that ended step j - 1).  At the top of step j every copy of this wave
+    // (tile j's, and the Q loads before the first) has landed.
     for (int j = 0; j < Tc; ++j) {
         const int buf = j & 1;
-        if (j + 1 < Tc) {
-            issue_tile(j + 1, buf ^ 1);
-            wait_vmcnt<B16_LOADS>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_vmcnt<0>();
         lds_barrier();
+        __amdgpu_buffer_rsrc_t nrk, nrv;
+        tile_rsrc(j + 1, nrk, nrv);
 
         const int kv_start = j * B16_BC;
         // A tile entirely above this wave's rows (causal) is computed anyway:
@@ -212,6 +217,12 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
             static_for<B16_PF>([&](auto i) { rd_k(i); });
+            // The two waves of a SIMD alternate between MFMA phases and the
+            // softmax; the wave in an MFMA phase gets issue priority, so the
+            // matrix pipe is fed first and the other wave's VALU work fills
+            // the gaps.
+            __builtin_amdgcn_s_setprio(2);
+            static_assert(KS == B16_LOADS, "one tile copy per score k-step");
             static_for<KS>([&](auto kk_c) {
                 constexpr int kk = decltype(kk_c)::value;
                 if constexpr (kk + B16_PF < KS) rd_k(std::integral_constant<int, kk + B16_PF>{});
@@ -219,9 +230,11 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                 wait_lgkm_for<newer>(fa[kk % (B16_PF + 1)], fb[kk % (B16_PF + 1)]);
                 __builtin_amdgcn_sched_barrier(0);
                 s0 = mfma32(fa[kk % (B16_PF + 1)], qf[kk], s0);
+                issue_copy(kk_c, nrk, nrv, buf ^ 1);
                 s1 = mfma32(fb[kk % (B16_PF + 1)], qf[kk], s1);
                 __builtin_amdgcn_sched_barrier(0);
             });
+            __builtin_amdgcn_s_setprio(0);
             // The first V^T fragments are requested before the softmax so that
             // its arithmetic covers their latency.
             bf16x8 fv[B16_PFV + 1];
@@ -275,6 +288,7 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                     pb[(e >> 3)][e & 7] = to_bf16(p0);
                     pb[2 + (e >> 3)][e & 7] = to_bf16(p1);
                 }
+                __builtin_amdgcn_s_setprio(2);
                 static_for<PS>([&](auto st_c) {
                     constexpr int st = decltype(st_c)::value;
                     constexpr int ks = st / 4, db = st % 4;
@@ -285,6 +299,7 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
                     oacc[db] = mfma32(fv[st % (B16_PFV + 1)], pb[ks], oacc[db]);
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                __builtin_amdgcn_s_setprio(0);
             };
             // Lazy rescale (see kRescaleSlack): the base moves only when a
             // row max exceeds it by more than the slack.
@@ -306,6 +321,9 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
         }
         lds_barrier();
     }
+    // The last step's (empty) copies must land before the workgroup's LDS is
+    // released.
+    wait_vmcnt<0>();
 
     // Epilogue: O = Oacc / l; O^T register e of block db: dim 32db + 8(e/4) + 4g + e%4.
     l = sum2_halves(l);
