@@ -200,8 +200,10 @@ def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007):
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma"}
 
 
+# The decode kernels, their plan layout, and the host code that sets the plan
+# constants (the split count, and with it the partial traffic, depends on them).
 DECODE_SOURCES = ("mla_latent_kv_attn_amd/csrc/mla_decode.hip", "mla_latent_kv_attn_amd/csrc/mla_plan.h",
-                  "mla_latent_kv_attn_amd/csrc/common.h")
+                  "mla_latent_kv_attn_amd/csrc/common.h", "mla_latent_kv_attn_amd/csrc/api.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_varlen_pmc.json")
 
 
