@@ -5,15 +5,23 @@
 // the per-row log-sum-exp.  The structure follows the blog's v2 loop order
 // (section 1.1: query tile outer, key/value tiles inner, one workgroup per
 // (query tile, batch*head)) with these MI355X choices:
-//   * one query row per lane, as in the blog, but the query row and the
-//     unnormalised accumulator live in VGPRs (64 + 64 floats per lane)
-//     instead of shared memory -- the blog's section 4.2 attributes its
-//     remaining stall to the 66KB of Qs+Oacc in shared memory capping
-//     occupancy;
+//   * lanes l and l + 32 of a wave share two query rows: lane l holds dims
+//     0..31 and lane l + 32 dims 32..63 of both rows, for the query and for
+//     the unnormalised accumulator (64 + 64 floats per lane, in VGPRs rather
+//     than shared memory -- the blog's section 4.2 attributes its remaining
+//     stall to the 66KB of Qs+Oacc in shared memory capping occupancy).
+//     Every 16-byte K or V read from LDS then feeds 8 FMAs instead of 4: with
+//     one row per lane the broadcast LDS reads, one per 4 FMAs, limited the
+//     kernel as much as the FMA pipe did;
+//   * one v_permlane32_swap and one add per key complete both rows' scores:
+//     afterwards lane l holds the score of the first row and lane l + 32 that
+//     of the second, so each lane runs the softmax of one row (one exp per
+//     key and lane), and a second swap hands each lane both rows' P for the
+//     value product;
 //   * K/V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
 //     register staging) into a double buffer (the cp.async double buffer of
 //     section 3.2); rows past N are clamped to row N-1 and masked to -inf;
-//   * every lane of a wave reads the same K/V row, so LDS reads are
+//   * all lanes of a wave half read the same K/V address, so LDS reads are
 //     broadcasts and need no padding (section 3.1 makes the same point);
 //   * the score is kept in the log2 domain (scale * log2(e) folded into Q)
 //     and exponentials use v_exp_f32;
@@ -26,10 +34,20 @@
 namespace mla {
 
 constexpr int F32_D = 64;
-constexpr int F32_BR = 128;  // query rows per workgroup (one per lane)
-constexpr int F32_BC = 32;   // keys per tile
-constexpr int F32_THREADS = F32_BR;
+constexpr int F32_DH = F32_D / 2;  // dims per lane
+constexpr int F32_BR = 128;        // query rows per workgroup (64 per wave, two per lane pair)
+constexpr int F32_BC = 32;         // keys per tile
+constexpr int F32_THREADS = 128;
 constexpr int F32_LOADS_PER_WAVE = (F32_BC * F32_D * 4) / (16 * 64) / (F32_THREADS / 64);  // per K (or V) tile
+
+// v_permlane32_swap(x, y) swaps the upper 32 lanes of x with the lower 32
+// lanes of y.  Afterwards lane l < 32 holds (its own x, x of lane l + 32) and
+// lane l + 32 holds (y of lane l, its own y).
+__device__ __forceinline__ void swap_halves(float& x, float& y) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
@@ -51,24 +69,34 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
     // Causal mask aligned at the bottom right: row i sees keys <= i + off.
     const int off = Nk - Nq;
 
-    const int tid = threadIdx.x;
     const int w = wave_id();
     const int lane = lane_id();
-    const int row = q_start + tid;
-    const bool row_valid = row < Nq;
-    const int row_c = row_valid ? row : (Nq - 1);
-
-    // Query row into registers, pre-scaled into the log2 domain.
-    float qr[F32_D];
-    {
-        const float4* qp = reinterpret_cast<const float4*>(q + base + (size_t)row_c * F32_D);
+    const int half = lane >> 5;  // which 32 dims this lane holds
+    const int pr = lane & 31;    // lane pair
+    // The pair's rows: r[0] = base row + pr, r[1] = r[0] + 32.  The lane's
+    // own row (the one whose softmax it runs) is r[half].
+    int rows[2], rows_c[2];
 #pragma unroll
-        for (int i = 0; i < F32_D / 4; ++i) {
+    for (int j = 0; j < 2; ++j) {
+        rows[j] = q_start + 64 * w + 32 * j + pr;
+        rows_c[j] = rows[j] < Nq ? rows[j] : (Nq - 1);
+    }
+    const int my_row = half ? rows[1] : rows[0];
+    const int my_row_c = half ? rows_c[1] : rows_c[0];
+
+    // Query rows into registers (this lane's 32 dims of both rows),
+    // pre-scaled into the log2 domain.
+    float qr[2][F32_DH];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float4* qp = reinterpret_cast<const float4*>(q + base + (size_t)rows_c[j] * F32_D + F32_DH * half);
+#pragma unroll
+        for (int i = 0; i < F32_DH / 4; ++i) {
             float4 t = qp[i];
-            qr[4 * i + 0] = t.x * scale_log2;
-            qr[4 * i + 1] = t.y * scale_log2;
-            qr[4 * i + 2] = t.z * scale_log2;
-            qr[4 * i + 3] = t.w * scale_log2;
+            qr[j][4 * i + 0] = t.x * scale_log2;
+            qr[j][4 * i + 1] = t.y * scale_log2;
+            qr[j][4 * i + 2] = t.z * scale_log2;
+            qr[j][4 * i + 3] = t.w * scale_log2;
         }
     }
 
@@ -92,46 +120,59 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
         }
     };
 
-    float oacc[F32_D];
+    float oacc[2][F32_DH];
 #pragma unroll
-    for (int d = 0; d < F32_D; ++d) oacc[d] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int d = 0; d < F32_DH; ++d) oacc[j][d] = 0.f;
+    float m = -INFINITY, l = 0.f;  // of this lane's own row
 
     if (Tc > 0) issue_tile(0, 0);
-    for (int j = 0; j < Tc; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < Tc) {
-            issue_tile(j + 1, buf ^ 1);
+    for (int jt = 0; jt < Tc; ++jt) {
+        const int buf = jt & 1;
+        if (jt + 1 < Tc) {
+            issue_tile(jt + 1, buf ^ 1);
             wait_vmcnt<2 * F32_LOADS_PER_WAVE>();
         } else {
             wait_vmcnt<0>();
         }
         lds_barrier();
 
-        const int kv_start = j * F32_BC;
-        const float4* Kt = reinterpret_cast<const float4*>(Ks[buf]);
-        const float4* Vt = reinterpret_cast<const float4*>(Vs[buf]);
+        const int kv_start = jt * F32_BC;
+        // This lane's 32 dims of each K / V row start at float4 8 * half.
+        const float4* Kt = reinterpret_cast<const float4*>(Ks[buf]) + (F32_DH / 4) * half;
+        const float4* Vt = reinterpret_cast<const float4*>(Vs[buf]) + (F32_DH / 4) * half;
 
+        // Scores: partial dot products over this lane's dims for both rows,
+        // completed by one swap and one add per key.  Afterwards s[c] is the
+        // score of this lane's own row.
         float s[F32_BC];
 #pragma unroll
         for (int c = 0; c < F32_BC; ++c) {
-            float acc = 0.f;
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < F32_D / 4; ++i) {
-                float4 kk = Kt[c * (F32_D / 4) + i];
-                acc = __builtin_fmaf(qr[4 * i + 0], kk.x, acc);
-                acc = __builtin_fmaf(qr[4 * i + 1], kk.y, acc);
-                acc = __builtin_fmaf(qr[4 * i + 2], kk.z, acc);
-                acc = __builtin_fmaf(qr[4 * i + 3], kk.w, acc);
+            for (int i = 0; i < F32_DH / 4; ++i) {
+                const float4 kk = Kt[c * (F32_D / 4) + i];
+                a0 = __builtin_fmaf(qr[0][4 * i + 0], kk.x, a0);
+                a1 = __builtin_fmaf(qr[1][4 * i + 0], kk.x, a1);
+                a0 = __builtin_fmaf(qr[0][4 * i + 1], kk.y, a0);
+                a1 = __builtin_fmaf(qr[1][4 * i + 1], kk.y, a1);
+                a0 = __builtin_fmaf(qr[0][4 * i + 2], kk.z, a0);
+                a1 = __builtin_fmaf(qr[1][4 * i + 2], kk.z, a1);
+                a0 = __builtin_fmaf(qr[0][4 * i + 3], kk.w, a0);
+                a1 = __builtin_fmaf(qr[1][4 * i + 3], kk.w, a1);
             }
-            s[c] = acc;
+            // Lower lane: (own row-0 partial, upper's row-0 partial);
+            // upper lane: (lower's row-1 partial, own row-1 partial).
+            swap_halves(a0, a1);
+            s[c] = a0 + a1;
         }
         // Masks: keys past N only on the last tile; causal element mask only
         // on tiles that straddle the diagonal (section 3.4).
         const bool tail = kv_start + F32_BC > Nk;
         const bool diag = CAUSAL && (kv_start + F32_BC - 1 > q_start + off);
         if (tail || diag) {
-            const int lim = diag ? min(row_c + off + 1, Nk) : Nk;
+            const int lim = diag ? min(my_row_c + off + 1, Nk) : Nk;
 #pragma unroll
             for (int c = 0; c < F32_BC; ++c)
                 if (kv_start + c >= lim) s[c] = -INFINITY;
@@ -141,42 +182,58 @@ __global__ __launch_bounds__(F32_THREADS, 2) void attn_fwd_f32_kernel(
         for (int c = 1; c < F32_BC; ++c) mt = fmaxf(mt, s[c]);
         const float m_new = fmaxf(m, mt);
         const float mb = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m - mb);
+        float alpha0 = fast_exp2(m - mb), alpha1 = alpha0;
         float ls = 0.f;
 #pragma unroll
         for (int c = 0; c < F32_BC; ++c) {
             s[c] = fast_exp2(s[c] - mb);
             ls += s[c];
         }
-        l = l * alpha + ls;
+        l = l * alpha0 + ls;
         m = m_new;
+        // Both rows' rescale factors in every lane: (row 0, row 1).
+        swap_halves(alpha0, alpha1);
 #pragma unroll
-        for (int d = 0; d < F32_D; ++d) oacc[d] *= alpha;
+        for (int d = 0; d < F32_DH; ++d) {
+            oacc[0][d] *= alpha0;
+            oacc[1][d] *= alpha1;
+        }
 #pragma unroll
         for (int c = 0; c < F32_BC; ++c) {
-            const float p = s[c];
+            float p0 = s[c], p1 = s[c];
+            swap_halves(p0, p1);  // (row 0, row 1) in every lane
 #pragma unroll
-            for (int i = 0; i < F32_D / 4; ++i) {
-                float4 vv = Vt[c * (F32_D / 4) + i];
-                oacc[4 * i + 0] = __builtin_fmaf(p, vv.x, oacc[4 * i + 0]);
-                oacc[4 * i + 1] = __builtin_fmaf(p, vv.y, oacc[4 * i + 1]);
-                oacc[4 * i + 2] = __builtin_fmaf(p, vv.z, oacc[4 * i + 2]);
-                oacc[4 * i + 3] = __builtin_fmaf(p, vv.w, oacc[4 * i + 3]);
+            for (int i = 0; i < F32_DH / 4; ++i) {
+                const float4 vv = Vt[c * (F32_D / 4) + i];
+                oacc[0][4 * i + 0] = __builtin_fmaf(p0, vv.x, oacc[0][4 * i + 0]);
+                oacc[1][4 * i + 0] = __builtin_fmaf(p1, vv.x, oacc[1][4 * i + 0]);
+                oacc[0][4 * i + 1] = __builtin_fmaf(p0, vv.y, oacc[0][4 * i + 1]);
+                oacc[1][4 * i + 1] = __builtin_fmaf(p1, vv.y, oacc[1][4 * i + 1]);
+                oacc[0][4 * i + 2] = __builtin_fmaf(p0, vv.z, oacc[0][4 * i + 2]);
+                oacc[1][4 * i + 2] = __builtin_fmaf(p1, vv.z, oacc[1][4 * i + 2]);
+                oacc[0][4 * i + 3] = __builtin_fmaf(p0, vv.w, oacc[0][4 * i + 3]);
+                oacc[1][4 * i + 3] = __builtin_fmaf(p1, vv.w, oacc[1][4 * i + 3]);
             }
         }
         lds_barrier();
     }
 
-    if (row_valid) {
-        // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
-        const float inv_l = l > 0.f ? 1.f / l : 0.f;
-        float4* op = reinterpret_cast<float4*>(o + base + (size_t)row * F32_D);
+    // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
+    const float inv_own = l > 0.f ? 1.f / l : 0.f;
+    float inv0 = inv_own, inv1 = inv_own;
+    swap_halves(inv0, inv1);  // (row 0, row 1) in every lane
 #pragma unroll
-        for (int i = 0; i < F32_D / 4; ++i)
-            op[i] = make_float4(oacc[4 * i] * inv_l, oacc[4 * i + 1] * inv_l, oacc[4 * i + 2] * inv_l,
-                                oacc[4 * i + 3] * inv_l);
-        if (lse) lse[(size_t)bh * Nq + row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
+    for (int j = 0; j < 2; ++j) {
+        if (rows[j] < Nq) {
+            const float inv = j ? inv1 : inv0;
+            float4* op = reinterpret_cast<float4*>(o + base + (size_t)rows[j] * F32_D + F32_DH * half);
+#pragma unroll
+            for (int i = 0; i < F32_DH / 4; ++i)
+                op[i] = make_float4(oacc[j][4 * i] * inv, oacc[j][4 * i + 1] * inv, oacc[j][4 * i + 2] * inv,
+                                    oacc[j][4 * i + 3] * inv);
+        }
     }
+    if (lse && my_row < Nq) lse[(size_t)bh * Nq + my_row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
 }
 
 // Host-side launcher (called by the C ABI after validation).
