@@ -35,9 +35,13 @@ namespace mla {
 
 constexpr int F32_D = 64;
 constexpr int F32_DH = F32_D / 2;  // dims per lane
-constexpr int F32_BR = 128;        // query rows per workgroup (64 per wave, two per lane pair)
+// A workgroup is 4 waves (one per SIMD) and 256 query rows.  With 2-wave,
+// 128-row workgroups the start stamps of the workgroups showed only about
+// three of them resident per CU (6 of the 8 wave slots that the register
+// count allows), and the non-causal kernel took 1.5x longer.
+constexpr int F32_BR = 256;        // query rows per workgroup (64 per wave, two per lane pair)
 constexpr int F32_BC = 32;         // keys per tile
-constexpr int F32_THREADS = 128;
+constexpr int F32_THREADS = 256;
 constexpr int F32_LOADS_PER_WAVE = (F32_BC * F32_D * 4) / (16 * 64) / (F32_THREADS / 64);  // per K (or V) tile
 
 // v_permlane32_swap(x, y) swaps the upper 32 lanes of x with the lower 32
