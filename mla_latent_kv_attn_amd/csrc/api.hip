@@ -70,7 +70,9 @@ DecodeConfig decode_config(int B, int num_splits, int cus) {
         c.slots = 0;
     } else {
         long long p = (long long)B * num_splits;
-        c.parts = (int)(p < cus ? p : cus);
+        if (p > cus) p = cus;
+        if (p > mla::kPlanMaxParts) p = mla::kPlanMaxParts;
+        c.parts = (int)p;
         c.slots = 2 * c.parts;
     }
     return c;

@@ -87,47 +87,88 @@ struct PlanArgs {
 //      t = max(ceil(C / parts), ceil(max_n / (num_splits - 1)), t_min, 1),
 //    which bounds every sequence to at most num_splits parts.  With
 //    num_splits == 1 each sequence gets its own part (t = max_n + c0).
+//    One workgroup of 256 threads; each thread handles four consecutive
+//    sequences of a 1024-sequence chunk, so the offsets need one scan per
+//    chunk (within each wave by lane shuffles, then over the four wave
+//    totals).  The first sequence of each part is found with LDS atomics.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ seqlens, int* __restrict__ ws,
-                                                       int B, int S_max, int parts, int c0, int t_min,
-                                                       int num_splits, PlanArgs a) {
-    __shared__ int scan[1024];
-    __shared__ int s_max, s_clamp, s_carry;
-    const int tid = threadIdx.x;
-    if (tid == 0) { s_max = 0; s_clamp = 0; s_carry = 0; }
-    __syncthreads();
-    int my_n = 0, my_start = 0;  // sequence tid's entries (used when B <= 1024)
-    for (int base = 0; base < B; base += 1024) {
-        const int b = base + tid;
-        int cost = 0;
-        if (b < B) {
-            const int raw = seqlens[b];
-            const int len = min(max(raw, 0), S_max);
-            if (len != raw) atomicAdd(&s_clamp, 1);
-            const int n = (len + kDecodeTile - 1) / kDecodeTile;
-            cost = n > 0 ? n + c0 : 0;
-            ws[a.seq_len + b] = len;
-            ws[a.seq_n + b] = n;
-            my_n = n;
-            atomicMax(&s_max, n);
-        }
-        scan[tid] = cost;
-        __syncthreads();
-        for (int d = 1; d < 1024; d <<= 1) {
-            const int add = tid >= d ? scan[tid - d] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
-        }
-        if (b < B) {
-            my_start = s_carry + scan[tid] - cost + c0;
-            ws[a.seq_start + b] = my_start;
-        }
-        __syncthreads();
-        if (tid == 0) s_carry += scan[1023];
-        __syncthreads();
+constexpr int PLAN_THREADS = 256;
+constexpr int PLAN_PER = 4;
+constexpr int PLAN_CHUNK = PLAN_THREADS * PLAN_PER;
+
+__device__ __forceinline__ int wave_incl_sum(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
     }
-    const int max_n = s_max;
+    return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(const int* __restrict__ seqlens, int* __restrict__ ws,
+                                                               int B, int S_max, int parts, int c0, int t_min,
+                                                               int num_splits, PlanArgs a) {
+    __shared__ int s_wsum[PLAN_THREADS / 64], s_wmax[PLAN_THREADS / 64], s_wclamp[PLAN_THREADS / 64];
+    __shared__ int s_pfs[kPlanMaxParts];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int my_n[PLAN_PER], my_start[PLAN_PER];  // kept for the second pass when B <= PLAN_CHUNK
+    int carry = 0, mx = 0, nclamp = 0;
+    for (int base = 0; base < B; base += PLAN_CHUNK) {
+        int cost[PLAN_PER], sum = 0;
+#pragma unroll
+        for (int k = 0; k < PLAN_PER; ++k) {
+            const int b = base + PLAN_PER * tid + k;
+            int n = 0;
+            if (b < B) {
+                const int raw = seqlens[b];
+                const int len = min(max(raw, 0), S_max);
+                nclamp += len != raw;
+                n = (len + kDecodeTile - 1) / kDecodeTile;
+                ws[a.seq_len + b] = len;
+                ws[a.seq_n + b] = n;
+                mx = max(mx, n);
+            }
+            my_n[k] = n;
+            cost[k] = n > 0 ? n + c0 : 0;
+            sum += cost[k];
+        }
+        const int incl = wave_incl_sum(sum, lane);
+        if (lane == 63) s_wsum[wv] = incl;
+        __syncthreads();
+        int woff = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < PLAN_THREADS / 64; ++i) {
+            woff += i < wv ? s_wsum[i] : 0;
+            total += s_wsum[i];
+        }
+        __syncthreads();  // s_wsum is rewritten by the next chunk
+        int acc = carry + woff + incl - sum;  // cost of all sequences before this thread's first
+#pragma unroll
+        for (int k = 0; k < PLAN_PER; ++k) {
+            const int b = base + PLAN_PER * tid + k;
+            my_start[k] = acc + c0;
+            if (b < B) ws[a.seq_start + b] = my_start[k];
+            acc += cost[k];
+        }
+        carry += total;
+    }
+    mx = wave_max(mx);
+    nclamp = wave_sum(nclamp);
+    if (lane == 0) { s_wmax[wv] = mx; s_wclamp[wv] = nclamp; }
+    __syncthreads();
+    int max_n = 0, clamped = 0;
+#pragma unroll
+    for (int i = 0; i < PLAN_THREADS / 64; ++i) { max_n = max(max_n, s_wmax[i]); clamped += s_wclamp[i]; }
     const bool whole = num_splits == 1;
     int t, C, parts_used, nparts;
     if (whole) {
@@ -136,27 +177,39 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
         parts_used = B;
         nparts = B;
     } else {
-        C = s_carry;
+        C = carry;
         t = max(max((C + parts - 1) / parts, (max_n + num_splits - 2) / (num_splits - 1)), max(t_min, 1));
         parts_used = (C + t - 1) / t;
-        nparts = parts;
+        nparts = parts;  // <= kPlanMaxParts (checked by the host)
+        for (int p = tid; p < nparts; p += PLAN_THREADS) s_pfs[p] = B;
     }
-    for (int p = tid; p < nparts; p += 1024) ws[a.part_first_seq + p] = B;
     __syncthreads();
-    for (int b = tid; b < B; b += 1024) {
-        // With one chunk the entries are still in registers; otherwise they
-        // are read back (this thread wrote them above).
-        const int n = B <= 1024 ? my_n : ws[a.seq_n + b];
-        int start = B <= 1024 ? my_start : ws[a.seq_start + b];
-        if (whole) {
-            start = b * t + c0;
-            ws[a.seq_start + b] = start;
+    for (int base = 0; base < B; base += PLAN_CHUNK) {
+#pragma unroll
+        for (int k = 0; k < PLAN_PER; ++k) {
+            const int b = base + PLAN_PER * tid + k;
+            if (b >= B) continue;
+            // With one chunk the entries are still in registers; otherwise
+            // they are read back (this thread wrote them above).
+            const int n = B <= PLAN_CHUNK ? my_n[k] : ws[a.seq_n + b];
+            int start = B <= PLAN_CHUNK ? my_start[k] : ws[a.seq_start + b];
+            if (whole) {
+                // Part b holds sequence b alone (t >= max_n + c0 > c0 + n - 1).
+                start = b * t + c0;
+                ws[a.seq_start + b] = start;
+                ws[a.part_first_seq + b] = n > 0 ? b : B;
+            }
+            const int first = n > 0 ? start / t : 0;
+            const int ns = n > 0 ? (start + n - 1) / t - first + 1 : 0;
+            ws[a.seq_first + b] = first;
+            ws[a.seq_nsplit + b] = ns;
+            if (!whole)
+                for (int p = first; p < first + ns; ++p) atomicMin(&s_pfs[p], b);
         }
-        const int first = n > 0 ? start / t : 0;
-        const int ns = n > 0 ? (start + n - 1) / t - first + 1 : 0;
-        ws[a.seq_first + b] = first;
-        ws[a.seq_nsplit + b] = ns;
-        for (int p = first; p < first + ns; ++p) atomicMin(&ws[a.part_first_seq + p], b);
+    }
+    if (!whole) {
+        __syncthreads();
+        for (int p = tid; p < nparts; p += PLAN_THREADS) ws[a.part_first_seq + p] = s_pfs[p];
     }
     if (tid == 0) {
         ws[kHdrPartsUsed] = parts_used;
@@ -166,7 +219,7 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int* __restrict__ 
         ws[kHdrC0] = c0;
         ws[kHdrMode] = whole ? 1 : 0;
         ws[kHdrParts] = nparts;
-        ws[kHdrClamped] = s_clamp;
+        ws[kHdrClamped] = clamped;
         ws[kHdrMaxN] = max_n;
         ws[kHdrB] = B;
         ws[kHdrTMin] = t_min;
@@ -870,7 +923,7 @@ hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __
     if (e != hipSuccess) return e;
     int* ws = static_cast<int*>(workspace);
     const PlanArgs a = plan_args(L);
-    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, seqlens, ws, B, S_max, L.parts, c0, t_min,
+    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, seqlens, ws, B, S_max, L.parts, c0, t_min,
                        num_splits, a);
     DecodeCtx x;
     x.q_lat = q_lat;

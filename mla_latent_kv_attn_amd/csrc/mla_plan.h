@@ -18,6 +18,7 @@ constexpr int kRope = 64;
 constexpr int kRow = kLatent + kRope;  // 576 bf16 per cached token
 constexpr int kMaxSplits = 32;
 constexpr int kMaxBatch = 1 << 16;
+constexpr int kPlanMaxParts = 1024;  // split-kernel parts in line mode (one per CU, capped)
 
 // Header words (int32) at the start of the workspace.
 enum PlanWord {
