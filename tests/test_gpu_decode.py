@@ -83,6 +83,26 @@ def test_decode_small(case, num_splits):
             assert torch.all(o[b] == 0) and torch.all(torch.isneginf(l[b]))
 
 
+@pytest.mark.parametrize("num_splits", [1, 8])
+def test_decode_many_short_sequences(num_splits):
+    # More sequences than the planner handles in one pass (1024 per chunk),
+    # many of them empty: the plan is checked whole, outputs on a sample.
+    B, H, S = 2500, 16, 100
+    lens = workloads.random_seqlens(B, 0, S, 2200).tolist()
+    say(f"decode B={B} H={H} lengths 0..{S} num_splits={num_splits}")
+    d = workloads.decode_inputs(B, H, lens, S_max=S, seed=2201)
+    o, l, ws = decode(d, num_splits)
+    check_plan(ws, d, num_splits)
+    empty = [b for b, L in enumerate(lens) if L == 0]
+    assert empty, "the sample should hold empty sequences"
+    assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(l[empty]))
+    rng = np.random.default_rng(2202)
+    idx = sorted(set(rng.choice(B, 96, replace=False).tolist()) | {0, 1023, 1024, B - 1, empty[0]})
+    Or, Lr = oracle_decode(d, idx)
+    check_bf16(o[idx], Or, "O(sampled)")
+    check_lse(l[idx], Lr, "LSE(sampled)")
+
+
 def test_decode_identical_rows_and_single_token():
     H = 128
     d = workloads.decode_inputs(3, H, [300, 1, 64], S_max=300, seed=2100)
