@@ -14,7 +14,10 @@
 // (v_mfma_f32_16x16x32_bf16): A = W^T fragments read with ds_read_b64_tr_b16
 // from the row-major slab, B = q_nope rows read straight from global memory
 // (16 contiguous bytes per lane), so each lane ends with 4 consecutive
-// latent columns of one row and stores them as 8 bytes.
+// latent columns of one row.  A wave's 16 x 128 output block goes through
+// LDS so that each store instruction writes four whole 256-byte rows: the
+// kernel is bound by its 34 MB of output writes, and 32-byte store segments
+// (16 per instruction) cost ~13% more time than whole rows.
 //
 // The Dl / 128 workgroups of one head read the same q_nope rows.  Work is
 // dealt to the 8 XCDs round-robin in dispatch order, so the block index is
@@ -90,6 +93,32 @@ __device__ __forceinline__ void abs_store(__bf16* q_lat, const f32x4 (&acc)[ABS_
     }
 }
 
+// Stores a wave's 16 rows x 128 columns through LDS (272-byte rows), so that
+// each global store instruction writes four whole 256-byte rows.
+constexpr int ABS_STG_STRIDE = 272;
+constexpr int ABS_STG_BYTES = 16 * ABS_STG_STRIDE;  // per wave
+__device__ __forceinline__ void abs_store_staged(__bf16* q_lat, const f32x4 (&acc)[ABS_COLS / 16], int b0, int B,
+                                                 int H, int h, int Dl, int col0, char* stg, int n, int g, int lane) {
+#pragma unroll
+    for (int db = 0; db < ABS_COLS / 16; ++db) {
+        bf16x4 t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = to_bf16(acc[db][r]);
+        *reinterpret_cast<bf16x4*>(stg + n * ABS_STG_STRIDE + 32 * db + 8 * g) = t;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): the wave's LDS writes landed
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = 4 * k + (lane >> 4), c = lane & 15;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * ABS_STG_STRIDE + 16 * c);
+        const int b = b0 + r;
+        if (b < B) *reinterpret_cast<bf16x8*>(q_lat + ((size_t)b * H + h) * Dl + col0 + 8 * c) = v;
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before the next block's writes
+    __builtin_amdgcn_wave_barrier();
+}
+
 // KS > 0: Dn = 32 KS, and each row block's q_nope rows are loaded while the
 // previous block's MFMAs run.  KS == 0: any Dn, rows loaded per k-step.
 // (A 512-row slab fills 128 KiB of LDS: one workgroup per CU, so that
@@ -136,7 +165,8 @@ __global__ __launch_bounds__(ABS_THREADS, KS == 16 ? 1 : 2) void mla_absorb_kern
             for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) abs_kstep(smem, kk, g, jj, qd, cur[kk], acc);
-            abs_store(q_lat, acc, bb + 16 * w + n, b_hi, H, h, Dl, col0, g);
+            abs_store_staged(q_lat, acc, bb + 16 * w, b_hi, H, h, Dl, col0, smem + Dn * 256 + w * ABS_STG_BYTES, n, g,
+                             lane);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) cur[kk] = nxt[kk];
         }
@@ -170,7 +200,7 @@ static int abs_rows(int B, int H, int nc) {
 template <int KS>
 static hipError_t launch_abs(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
                              hipStream_t stream) {
-    const int smem = Dn * ABS_COLS * 2;
+    const int smem = Dn * ABS_COLS * 2 + 4 * ABS_STG_BYTES;
     if (smem > 64 * 1024) {
         hipError_t e = ensure_smem_attr((const void*)mla_absorb_kernel<KS>, smem);
         if (e != hipSuccess) return e;
