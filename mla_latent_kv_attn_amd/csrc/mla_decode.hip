@@ -230,6 +230,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(const int* __res
 // ---------------------------------------------------------------------------
 // 2. Split kernel
 // ---------------------------------------------------------------------------
+template <int OFF>
+__device__ __forceinline__ void ds_write8(uint32_t addr, const u32x2& v) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+
 struct DecodeCtx {
     const __bf16* q_lat;
     const __bf16* q_rope;
@@ -693,9 +699,18 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     }
     step(std::false_type{}, std::true_type{}, 0u, tile_a(ntiles - 1) + pv_off, 0u, 0, tile_rsrc(0), smem);
 
-    // Normalise and store: O^T block (i, h) holds dims 16i + 4g + 0..3 of
-    // head 16(2w+h) + n.
+    // Normalise and store.  O^T block (i, h) holds dims 16i + 4g + 0..3 of
+    // head 16(2w+h) + n.  The rows go through LDS (the ring is free once
+    // this piece's last copies have landed and every wave has finished its
+    // last value product), so that each global store writes one whole 1 KB
+    // head row.  Staging row stride 1040 B: the 8-byte writes of 32 lanes
+    // (16 heads x 2 lane groups) then hit 64 distinct banks.
+    wait_vmcnt<0>();
+    lds_barrier();
     mfma_result_wait();  // the accumulators are read below
+    constexpr int STG = 1040;
+    static_assert(DEC_WAVES * 32 * STG <= DEC_SMEM, "staging fits in the ring");
+    const uint32_t stg = smem_a + (uint32_t)(w * 32 * STG);
     static_for<2>([&](auto h_c) {
         constexpr int h = decltype(h_c)::value;
         const bool act = 2 * w + h < nhb;
@@ -711,28 +726,43 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
                 x.lse_part[(size_t)slot * H + head] = lse_v;
             }
         }
-        if (act) {
-            __bf16* obase;
-            if (nsplit == 1) {
-                obase = x.o + ((size_t)b * H + head) * kLatent;
-            } else {
-                const int slot = 2 * p + (first_in_part ? 0 : 1);
-                obase = x.o_part + ((size_t)slot * H + head) * kLatent;
-            }
-            obase += 4 * g;
-            static_for<DEC_NV>([&](auto i_c) {
-                constexpr int i = decltype(i_c)::value;
-                const f32x4 v = acc_get<2 * i + h>();
-                bf16x4 t;
+        uint32_t wa = stg + (uint32_t)((16 * h + n) * STG + 8 * g);
+        static_for<DEC_NV>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            const f32x4 v = acc_get<2 * i + h>();
+            bf16x4 t;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) t[r] = to_bf16(v[r] * il);
-                *reinterpret_cast<bf16x4*>(obase + 16 * i) = t;
+            for (int r = 0; r < 4; ++r) t[r] = to_bf16(v[r] * il);
+            const u32x2 u = __builtin_bit_cast(u32x2, t);
+            ds_write8<32 * i>(wa, u);
+        });
+    });
+    wait_lgkm<0>();
+    // Row r of the wave's staging area is head hblk + 32w + r.
+    __bf16* obase;
+    if (nsplit == 1) {
+        obase = x.o + ((size_t)b * H + hblk + 32 * w) * kLatent;
+    } else {
+        const int slot = 2 * p + (first_in_part ? 0 : 1);
+        obase = x.o_part + ((size_t)slot * H + hblk + 32 * w) * kLatent;
+    }
+    const uint32_t ra = stg + (uint32_t)(16 * lane);
+    static_for<2>([&](auto h_c) {
+        constexpr int h = decltype(h_c)::value;
+        if (2 * w + h < nhb) {
+            u32x4 rowv[16];
+            static_for<16>([&](auto r_c) {
+                constexpr int r = decltype(r_c)::value;
+                rowv[r] = ds_read_u32x4<(16 * h + r) * STG>(ra);
+            });
+            wait_lgkm<0>();
+            static_for<16>([&](auto r_c) {
+                constexpr int r = decltype(r_c)::value;
+                *reinterpret_cast<u32x4*>(obase + (size_t)(16 * h + r) * kLatent + 8 * lane) = rowv[r];
             });
         }
     });
-    // The next piece copies into slots that this piece's last value product
-    // read, and this piece's last (empty) copies must land first.
-    wait_vmcnt<0>();
+    // The next piece copies into the ring: every wave's staging reads first.
     lds_barrier();
 }
 
