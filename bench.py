@@ -188,10 +188,16 @@ def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     fn = lambda: binding.attn_fwd_chunk(q, k, v, 1.0 / math.sqrt(D), True, o=o, lse=lse)
-    for _ in range(20):
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(max(3, int(0.1 / est))):  # about 0.1 s of warm-up, as for the other prefill lines
         fn()
     torch.cuda.synchronize()
-    ms = time_events(fn, 50)
+    ms = time_events(fn, max(10, min(100, int(0.2 / est))))
     avg = sum(ms) / len(ms)
     tf = 4.0 * D * B * H * chunk_pairs(Nq, Nk, True) / (avg * 1e-3) / 1e12
     log(f"prefill chunk bf16 Nq={Nq} Nk={Nk}: {avg:.3f} ms, {tf:.1f} TFLOP/s ({100*tf/BF16_PEAK_TFLOPS:.1f}%)")
