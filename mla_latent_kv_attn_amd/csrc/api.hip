@@ -53,17 +53,17 @@ inline bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 // when num_splits == 1.  c0 charges each sequence the fixed cost of a piece:
 // loading its query block, filling and draining the tile pipeline, and
 // writing its output.  Timestamps per workgroup on MI355X (256 sequences of
-// 256..8192 tokens) put that cost at about 18 us, against about 1.8 us per
-// 32-token step, i.e. five 64-token tiles; c0 = 6 measured fastest among
-// 2, 4, 6, 8 and 11 (2 -> 6: 332 -> 321 us per call).  t_min keeps parts
-// from becoming so short that the fixed cost dominates.
+// 256..8192 tokens) put that cost at about 15 us, against about 1.9 us per
+// 32-token step, i.e. four 64-token tiles; c0 = 4 measured fastest among
+// 3, 4, 5 and 6 (308.6 us per call against 312.2 us for 6).  t_min keeps
+// parts from becoming so short that the fixed cost dominates.
 struct DecodeConfig {
     int parts, slots, c0, t_min;
 };
 
 DecodeConfig decode_config(int B, int num_splits, int cus) {
     DecodeConfig c;
-    c.c0 = 6;
+    c.c0 = 4;
     c.t_min = 4;
     if (num_splits == 1) {
         c.parts = B;
