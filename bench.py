@@ -10,6 +10,8 @@ value = KV-cache bytes read per step (sum of len_b x 1152 B) / step time,
         in GB/s (absorption included in the step time).
 roofline = the decode call alone (plan + split + combine, timed with HIP
         events on the stream the library launches on) against 8 TB/s.
+decode_fixed = the decode alone on 16 sequences x 4096 tokens (inputs
+        rotated over 8 copies so the Infinity Cache cannot serve them).
 prefill = bf16 causal prefill (B=4 H=16 N=4096 D=128) and the fp32
         vector-ALU prefill (B=4 H=8 N=8192 D=64), TFLOP/s vs their peaks.
 cpu_baseline = the fp64 oracle on a bounded sample of the same decode
@@ -44,7 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
-    ap.add_argument("--only", choices=["decode", "prefill_bf16", "prefill_fp32", "prefill_chunk", "copy"],
+    ap.add_argument("--only", choices=["decode", "decode_fixed", "prefill_bf16", "prefill_fp32", "prefill_chunk",
+                                       "copy"],
                     default=None,
                     help="run only one workload (for profiling); 'copy' is a plain 256 MiB device copy "
                          "used to calibrate the HBM byte counters")
@@ -166,6 +169,49 @@ def bench_prefill(log, name, causal, reps=None):
     return {"workload": f"{name} B={w['B']} H={w['H']} N={w['N']} D={w['D']} causal={int(causal)}",
             "ms": round(avg, 4), "tflops": round(tf, 2), "peak_tflops": peak, "frac": round(tf / peak, 4),
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
+
+
+def bench_decode_fixed(log, copies=8, reps=200):
+    """MLA decode on the fixed-length batch (16 sequences x 4096 tokens, 128
+    heads, num_splits 32).  Its 75.5 MB cache fits in the 256 MB Infinity
+    Cache, so successive calls rotate over `copies` separate copies of the
+    inputs (8 x 75.5 MB > 2 x 256 MB): every call reads its cache from HBM."""
+    import torch
+    from mla_latent_kv_attn_amd import binding, workloads
+    dev = "cuda:0"
+    w = workloads.mla_fixed_workload()
+    B, H = w["B"], w["H"]
+    kv_bytes = int(w["seqlens"].sum()) * 576 * 2
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(q_lat=w["q_lat"].to(dev), q_rope=w["q_rope"].to(dev), cache=w["cache"].to(dev),
+                         sl=w["seqlens"].to(dev), ws=binding.alloc_decode_workspace(B, H, 32, dev),
+                         o=torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev),
+                         lse=torch.empty((B, H), dtype=torch.float32, device=dev)))
+
+    def call(i):
+        d = sets[i % copies]
+        binding.mla_decode_fwd(d["q_lat"], d["q_rope"], d["cache"], d["sl"], w["scale"], 32, workspace=d["ws"],
+                               o=d["o"], lse=d["lse"])
+
+    for i in range(100):
+        call(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(st)
+        call(i)
+        b.record(st)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = sum(ms) / len(ms)
+    gbs = kv_bytes / (avg * 1e-3) / 1e9
+    log(f"decode mla_fixed (16 x 4096, rotating {copies} input copies): {avg*1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": "mla_fixed: B=16, H=128, 4096 tokens each, num_splits<=32, "
+                        f"{copies} rotating input copies (no Infinity Cache reuse)",
+            "us": round(avg * 1e3, 2), "kv_bytes": kv_bytes, "GB_s": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
 def chunk_pairs(Nq, Nk, causal):
@@ -300,12 +346,16 @@ def main():
     if args.only == "prefill_chunk":
         bench_prefill_chunk(log)
         return
+    if args.only == "decode_fixed":
+        bench_decode_fixed(log)
+        return
     if args.only == "prefill_fp32":
         bench_prefill(log, "attn_fp32", False, reps=args.steps)
         return
     d = bench_decode(args, log)
     if args.only == "decode":
         return
+    decode_fixed = bench_decode_fixed(log)
     prefill = {}
     if not args.no_prefill:
         prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True)
@@ -342,6 +392,7 @@ def main():
                                 "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
                                 "note": "timed after the step, not part of value"},
         "cpu_baseline": cpu,
+        "decode_fixed": decode_fixed,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
