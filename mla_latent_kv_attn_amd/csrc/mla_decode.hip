@@ -691,6 +691,11 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
         });
         step(std::true_type{}, std::false_type{}, qa, 0u, tile_a(0) + pv_off, tok_end - tok_lo, tile_rsrc(DEC_AHEAD),
              smem + (DEC_AHEAD % DEC_NBUF) * DEC_TILE_BYTES);
+        // The first tile always moves the exponent base (from -inf), but the
+        // accumulators are still zero: the rescale by alpha = 0 would leave
+        // them unchanged, so it is skipped (256 AGPR reads, multiplies and
+        // writes per wave and piece).
+        st.resc = false;
     }
     for (int j = 1; j < ntiles; ++j) {
         top(j);
