@@ -893,16 +893,21 @@ __global__ __launch_bounds__(CMB_THREADS) void mla_combine_slots_kernel(const in
                                                                        __bf16* __restrict__ o, float* lse, int H,
                                                                        PlanArgs a) {
     const int b = blockIdx.x;
+    // All plan words are loaded before any of them is used: one round trip.
     const int ns = ws[a.seq_nsplit + b];
+    const int first = ws[a.seq_first + b];
+    const int start = ws[a.seq_start + b];
+    const int c0 = ws[kHdrC0], t = ws[kHdrT];
     if (ns == 1) return;
     const int hh = blockIdx.y * CMB_HEADS + (threadIdx.x >> 6);
     if (hh >= H) return;
     const int d8 = threadIdx.x & 63;
-    const int first = ws[a.seq_first + b];
     // Part `first` may begin with an earlier sequence (then b's piece is in
     // its second slot); every later part of b begins inside b, so b's piece
-    // there is in the part's first slot.
-    const int slot0 = 2 * first + (ws[a.part_first_seq + first] == b ? 0 : 1);
+    // there is in the part's first slot.  No earlier sequence has tiles in
+    // part `first` exactly when b's range on the cost line, which begins c0
+    // positions before its first tile, begins at or before the part does.
+    const int slot0 = 2 * first + (start - c0 <= first * t ? 0 : 1);
     auto rows = [&](int s) -> size_t { return (size_t)(s == 0 ? slot0 : 2 * (first + s)) * H + hh; };
     combine_head(o_part, lse_part, ns, rows, o + ((size_t)b * H + hh) * kLatent,
                  lse ? lse + (size_t)b * H + hh : nullptr, d8);

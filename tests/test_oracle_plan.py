@@ -63,6 +63,23 @@ def _random_case(seed):
 
 
 @pytest.mark.parametrize("seed", range(40))
+def test_first_piece_slot_from_line_position(seed):
+    # The combine finds the slot of a sequence's first piece without reading
+    # part_first_seq: sequence b is the first sequence of part first_b exactly
+    # when its range on the cost line (c0 positions, then its tiles) begins
+    # at or before that part.
+    seqlens, tile, parts, ns, c0, tmin = _random_case(seed)
+    plan = plan_ref(seqlens, tile, parts, ns, c0, tmin)
+    if plan["mode"] != "line":
+        return
+    for b in range(len(seqlens)):
+        if plan["n"][b] == 0:
+            continue
+        f = plan["first"][b]
+        assert (plan["part_first_seq"][f] == b) == (plan["start"][b] - plan["c0"] <= f * plan["t"]), b
+
+
+@pytest.mark.parametrize("seed", range(40))
 def test_plan_invariants_random(seed):
     seqlens, tile, parts, ns, c0, tmin = _random_case(seed)
     plan = plan_ref(seqlens, tile, parts, ns, c0, tmin)
