@@ -321,9 +321,35 @@ def cpu_baseline(d, log, budget_s=12.0):
         cores = len(os.sched_getaffinity(0))
     gbs = tbytes / elapsed / 1e9
     log(f"cpu oracle: {done} sequences, {tbytes/1e6:.1f} MB of cache in {elapsed:.2f} s -> {gbs:.3f} GB/s")
+    # The explicit-decompression check on a sample (4 sequences x 128 heads x
+    # their first 256 tokens): decode through decompressed keys against the
+    # absorbed decode, both in the oracle, timed separately.
+    qn = w["q_nope"][:4].float().numpy()
+    qr = w["q_rope"][:4].float().numpy()
+    cb = w["cache"][:4, :256].float().numpy()
+    sl = [min(256, lens[b]) for b in range(4)]
+    t0 = time.perf_counter()
+    o_exp, l_exp = oracle.mla_decode_explicit_ref(qn, qr, w_uk64, cb, sl, w["scale"])
+    t_exp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    o_abs, l_abs = oracle.mla_decode_ref(oracle.absorb_ref(qn, w_uk64), qr, cb, sl, w["scale"])
+    t_abs = time.perf_counter() - t0
+    diff = float(np.abs(o_exp - o_abs).max())
+    log(f"cpu oracle decompression check (4 seqs x 128 heads x 256 tokens): explicit {t_exp:.3f} s, "
+        f"absorbed {t_abs:.3f} s, max |dO| {diff:.2e}")
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"first {done} of 256 sequences of the decode workload ({tbytes} cache bytes), "
-                      f"absorption + decode in float64 numpy, {elapsed:.1f} s"}
+                      f"absorption + decode in float64 numpy, {elapsed:.1f} s",
+            "decompression_check": {"sample": "4 sequences x 128 heads x first 256 tokens",
+                                    "explicit_s": round(t_exp, 4), "absorbed_s": round(t_abs, 4),
+                                    "max_abs_diff_O": diff}}
 
 
 def main():
