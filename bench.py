@@ -138,7 +138,9 @@ def bench_decode(args, log):
     up_ms = a.elapsed_time(b) / 50
     up_bytes = (o.numel() + w_uv.numel() + o_v.numel()) * 2
     log(f"value up-projection: {up_ms*1e3:.1f} us ({up_bytes/(up_ms*1e-3)/1e9:.0f} GB/s)")
+    dec_sorted = sorted(dec_ms)
     return dict(workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
+                dec_median=dec_sorted[len(dec_sorted) // 2], dec_min=dec_sorted[0],
                 absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes)
 
 
@@ -162,12 +164,14 @@ def bench_prefill(log, name, causal, reps=None):
     torch.cuda.synchronize()
     ms = time_events(fn, reps or max(10, min(100, int(0.2 / est))))
     avg = sum(ms) / len(ms)
+    med, mn = sorted(ms)[len(ms) // 2], min(ms)
     fl = attn_flops(w["B"], w["H"], w["N"], w["D"], causal)
     tf = fl / (avg * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if w["dtype"] == torch.bfloat16 else FP32_VALU_PEAK_TFLOPS
     log(f"prefill {name} causal={causal}: {avg:.3f} ms, {tf:.1f} TFLOP/s ({100*tf/peak:.1f}% of {peak})")
     return {"workload": f"{name} B={w['B']} H={w['H']} N={w['N']} D={w['D']} causal={int(causal)}",
-            "ms": round(avg, 4), "tflops": round(tf, 2), "peak_tflops": peak, "frac": round(tf / peak, 4),
+            "ms": round(avg, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4), "tflops": round(tf, 2),
+            "peak_tflops": peak, "frac": round(tf / peak, 4),
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
 
 
@@ -412,7 +416,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "mla_decode_fwd (plan + split + combine kernels)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(log),
-                     "decode_us": round(d["dec_ms"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2)},
+                     "decode_us": round(d["dec_ms"] * 1e3, 2), "decode_us_median": round(d["dec_median"] * 1e3, 2),
+                     "decode_us_min": round(d["dec_min"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2)},
         "value_up_projection": {"workload": "o [256,128,512] @ W_UV [128,512,128] -> [256,128,128] bf16",
                                 "us": round(d["up_ms"] * 1e3, 2),
                                 "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
