@@ -103,6 +103,21 @@ def test_decode_many_short_sequences(num_splits):
     check_lse(l[idx], Lr, "LSE(sampled)")
 
 
+@pytest.mark.parametrize("num_splits", [8, 32])
+def test_decode_one_long_sequence(num_splits):
+    # One 32768-token sequence: it is split over up to num_splits parts and
+    # the combine merges that many partials.
+    L = 32768
+    say(f"decode B=1 H=128 len={L} num_splits={num_splits}")
+    d = workloads.decode_inputs(1, 128, [L], S_max=L, seed=2300)
+    o, l, ws = decode(d, num_splits)
+    plan = check_plan(ws, d, num_splits)
+    assert plan["nsplit"][0] == min(num_splits, plan["parts_used"])
+    Or, Lr = oracle_decode(d)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")
+
+
 def test_decode_identical_rows_and_single_token():
     H = 128
     d = workloads.decode_inputs(3, H, [300, 1, 64], S_max=300, seed=2100)
