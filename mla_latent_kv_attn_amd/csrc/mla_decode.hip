@@ -398,6 +398,10 @@ constexpr int DEC_LEAD = 4;
 constexpr int DEC_NVK = 9;
 constexpr int DEC_SMX_AT = 1;        // softmax starts at the first MFMA of group last_k + 1
 static_assert(DEC_LEAD >= DEC_D && 2 * (DEC_D - 1) < 16, "prefetch across the barrier; lgkmcnt range");
+// The softmax reads the tile's scores, which are complete only after the
+// MFMAs of the last K group: its first slice must come after that group
+// (with DEC_SMX_AT = 0 it would read unfinished accumulators).
+static_assert(DEC_SMX_AT >= 1, "softmax after the last score MFMA");
 static_assert(DEC_LEAD + DEC_NVK <= DEC_NV, "V groups");
 // Fragment registers are named per group (one name per group of a step):
 // every read is a new value, so the names cost no registers, and the V
