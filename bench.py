@@ -359,7 +359,7 @@ def cpu_baseline(d, log, budget_s=12.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     log = lambda s: print(s, file=sys.stderr, flush=True)
