@@ -118,6 +118,31 @@ def test_decode_one_long_sequence(num_splits):
     check_lse(l, Lr, "LSE")
 
 
+def test_decode_concurrent_streams_match_serial():
+    # The library keeps no state between calls: two decodes in flight at once
+    # on two streams (each with its own workspace) give the serial results.
+    H = 128
+    d1 = workloads.decode_inputs(6, H, [700, 64, 1500, 33, 0, 900], S_max=1500, seed=2400)
+    d2 = workloads.decode_inputs(4, H, [2000, 128, 1, 640], S_max=2000, seed=2401)
+    o1, l1, _ = decode(d1, 7)
+    o2, l2, _ = decode(d2, 32)
+    ins = []
+    for d, ns in ((d1, 7), (d2, 32)):
+        B = d["q_lat"].shape[0]
+        ins.append((d["q_lat"].to(DEV), d["q_rope"].to(DEV), d["cache"].to(DEV), d["seqlens"].to(DEV), ns,
+                    binding.alloc_decode_workspace(B, H, ns, DEV)))
+    sync()
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]  # default priority
+    outs = [None, None]
+    for rep in range(3):
+        for i, (ql, qr, c, sl, ns, ws) in enumerate(ins):
+            with torch.cuda.stream(streams[i]):
+                outs[i] = binding.mla_decode_fwd(ql, qr, c, sl, SCALE, ns, workspace=ws)
+        sync()
+        assert torch.equal(outs[0][0], o1) and torch.equal(outs[0][1], l1), rep
+        assert torch.equal(outs[1][0], o2) and torch.equal(outs[1][1], l2), rep
+
+
 def test_decode_identical_rows_and_single_token():
     H = 128
     d = workloads.decode_inputs(3, H, [300, 1, 64], S_max=300, seed=2100)
