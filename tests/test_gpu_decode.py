@@ -143,6 +143,47 @@ def test_decode_concurrent_streams_match_serial():
         assert torch.equal(outs[1][0], o2) and torch.equal(outs[1][1], l2), rep
 
 
+def test_decode_in_hip_graph_replays_match_eager():
+    # Nothing in the call allocates, frees, synchronises or sets memory, so
+    # absorption + decode can be captured in a HIP graph; every replay (with
+    # eager work and synchronisations between them) gives the eager result.
+    B, H, ns = 5, 128, 7
+    d = workloads.decode_inputs(B, H, [900, 1, 0, 2100, 333], S_max=2100, seed=2500)
+    g = torch.Generator().manual_seed(2501)
+    q_nope = torch.randn((B, H, 128), generator=g).to(torch.bfloat16).to(DEV)
+    w_uk = (torch.randn((H, 128, 512), generator=g) * 0.02).to(torch.bfloat16).to(DEV)
+    qr, c, sl = d["q_rope"].to(DEV), d["cache"].to(DEV), d["seqlens"].to(DEV)
+    ws = binding.alloc_decode_workspace(B, H, ns, DEV)
+    q_lat = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+
+    def step():
+        binding.mla_absorb_q(q_nope, w_uk, q_lat=q_lat)
+        binding.mla_decode_fwd(q_lat, qr, c, sl, SCALE, ns, workspace=ws, o=o, lse=lse)
+
+    step()
+    sync()
+    o_ref, l_ref = o.clone(), lse.clone()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        o.zero_()
+        lse.zero_()
+        q_lat.zero_()
+        sync()
+        graph.replay()
+        sync()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), rep
+
+
 def test_decode_identical_rows_and_single_token():
     H = 128
     d = workloads.decode_inputs(3, H, [300, 1, 64], S_max=300, seed=2100)
