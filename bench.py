@@ -297,6 +297,23 @@ def plain_copy():
     print(f"copied {n} bytes 3 times", file=sys.stderr, flush=True)
 
 
+def copy_bandwidth(log, nbytes=1 << 30, reps=20):
+    """Attainable HBM rate of a plain device copy (context for the roofline):
+    bytes read + bytes written per copy / time."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ms = time_events(lambda: b.copy_(a), reps)
+    avg = sum(ms) / len(ms)
+    gbs = 2 * nbytes / (avg * 1e-3) / 1e9
+    log(f"device copy of {nbytes >> 20} MiB: {avg*1e3:.1f} us, {gbs:.0f} GB/s (read + write)")
+    del a, b
+    return round(gbs, 1)
+
+
 def cpu_baseline(d, log, budget_s=12.0):
     """Time the oracle (as it stands) on a bounded sample of the decode workload."""
     import numpy as np
@@ -386,6 +403,7 @@ def main():
     if args.only == "decode":
         return
     decode_fixed = bench_decode_fixed(log)
+    copy_gbs = copy_bandwidth(log)
     prefill = {}
     if not args.no_prefill:
         prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True)
@@ -417,7 +435,8 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(log),
                      "decode_us": round(d["dec_ms"] * 1e3, 2), "decode_us_median": round(d["dec_median"] * 1e3, 2),
-                     "decode_us_min": round(d["dec_min"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2)},
+                     "decode_us_min": round(d["dec_min"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2),
+                     "attainable_copy_GB_s": copy_gbs},
         "value_up_projection": {"workload": "o [256,128,512] @ W_UV [128,512,128] -> [256,128,128] bf16",
                                 "us": round(d["up_ms"] * 1e3, 2),
                                 "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
