@@ -19,8 +19,11 @@ cpu_baseline = the fp64 oracle on a bounded sample of the same decode
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--no-cpu] [--no-prefill]
 
-The defaults warm up for 100 steps: the first few dozen decode calls after a
-start run 10-15% slower than the steady state (clock and cache ramp).
+Warm-up: besides the --warmup steps, every timed leg first runs its workload
+for a fixed time (--warm-seconds, default 2 s for the decode and 0.5 s for
+the others): the first calls after a start run slower than the steady state
+(the shader clock ramps up under load), however few steps --warmup asks for.
+The decode leg reports the seconds and calls it warmed up for.
 """
 
 import argparse
@@ -44,6 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warm-seconds", type=float, default=2.0,
+                    help="time-based warm-up of the decode leg before the --warmup steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     ap.add_argument("--only", choices=["decode", "decode_fixed", "prefill_bf16", "prefill_fp32", "prefill_chunk",
@@ -58,6 +63,20 @@ def attn_flops(B, H, N, D, causal):
     """Algorithmic FLOPs: 2 products of 2*D per visible (query, key) pair."""
     pairs = N * (N + 1) // 2 if causal else N * N
     return 4.0 * B * H * D * pairs
+
+
+def warm(fn, seconds, min_calls=3):
+    """Run fn until `seconds` of wall time have passed (and at least
+    min_calls times); returns (seconds, calls)."""
+    import torch
+    t0, calls = time.perf_counter(), 0
+    while True:
+        fn()
+        calls += 1
+        if calls % 8 == 0 or calls >= min_calls:
+            torch.cuda.synchronize()
+            if calls >= min_calls and time.perf_counter() - t0 >= seconds:
+                return time.perf_counter() - t0, calls
 
 
 def time_events(fn, reps):
@@ -98,9 +117,20 @@ def bench_decode(args, log):
         absorb()
         decode()
 
+    # Time-based warm-up to the steady state, then the --warmup steps.
+    warm_calls, t_w = 0, time.perf_counter()
+    while True:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        warm_calls += 50
+        if time.perf_counter() - t_w >= args.warm_seconds:
+            break
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
+    warm_calls += args.warmup
     st = torch.cuda.current_stream()
     ev = []
     t0 = time.perf_counter()
@@ -141,10 +171,45 @@ def bench_decode(args, log):
     dec_sorted = sorted(dec_ms)
     return dict(workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
                 dec_median=dec_sorted[len(dec_sorted) // 2], dec_min=dec_sorted[0],
-                absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes)
+                absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes,
+                warm_s=warm_s, warm_calls=warm_calls)
 
 
-def bench_prefill(log, name, causal, reps=None):
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((p.get("num_threads", 1) for p in threadpool_info()), default=1))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_prefill_oracle(log, q, k, v, scale, causal, what, budget_s=3.0):
+    """Time the prefill oracle (as it stands) on whole (b, h) slices of the
+    same CPU inputs, until about budget_s of CPU time; TFLOP/s counted with
+    the same algorithmic FLOPs as the GPU line."""
+    import numpy as np
+    import oracle
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    flops, elapsed, done = 0.0, 0.0, 0
+    for i in range(B * H):
+        b, h = i % B, (i * 5) % H
+        qs, ks, vs = (t[b:b + 1, h:h + 1].float().numpy().astype(np.float64) for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attn_ref(qs, ks, vs, scale, causal)
+        elapsed += time.perf_counter() - t0
+        flops += 4.0 * D * chunk_pairs(Nq, Nk, causal)
+        done += 1
+        if elapsed >= budget_s:
+            break
+    tf = flops / elapsed / 1e12
+    log(f"cpu oracle {what}: {done} (b,h) slices in {elapsed:.2f} s -> {tf*1e3:.2f} GFLOP/s")
+    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{done} whole (b,h) slices of {B * H} ({Nq} queries x {Nk} keys each), float64 numpy, "
+                      f"{elapsed:.1f} s"}
+
+
+def bench_prefill(log, name, causal, reps=None, cpu=False):
     import torch
     from mla_latent_kv_attn_amd import binding, workloads
     dev = "cuda:0"
@@ -153,15 +218,8 @@ def bench_prefill(log, name, causal, reps=None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fn = lambda: binding.attn_fwd(q, k, v, w["scale"], causal, o=o, lse=lse)
-    fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    fn()
-    torch.cuda.synchronize()
-    est = max(time.perf_counter() - t0, 1e-4)
-    for _ in range(max(3, int(0.1 / est))):  # about 0.1 s of warm-up
-        fn()
-    torch.cuda.synchronize()
+    ws, wc = warm(fn, 0.5)
+    est = ws / wc
     ms = time_events(fn, reps or max(10, min(100, int(0.2 / est))))
     avg = sum(ms) / len(ms)
     med, mn = sorted(ms)[len(ms) // 2], min(ms)
@@ -169,10 +227,15 @@ def bench_prefill(log, name, causal, reps=None):
     tf = fl / (avg * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if w["dtype"] == torch.bfloat16 else FP32_VALU_PEAK_TFLOPS
     log(f"prefill {name} causal={causal}: {avg:.3f} ms, {tf:.1f} TFLOP/s ({100*tf/peak:.1f}% of {peak})")
-    return {"workload": f"{name} B={w['B']} H={w['H']} N={w['N']} D={w['D']} causal={int(causal)}",
+    line = {"workload": f"{name} B={w['B']} H={w['H']} N={w['N']} D={w['D']} causal={int(causal)}",
             "ms": round(avg, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4), "tflops": round(tf, 2),
             "peak_tflops": peak, "frac": round(tf / peak, 4),
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
+    if cpu:
+        del q, k, v, o, lse
+        line["cpu_oracle"] = cpu_prefill_oracle(log, w["q"], w["k"], w["v"], w["scale"], causal,
+                                                f"{name} causal={int(causal)}")
+    return line
 
 
 def bench_decode_fixed(log, copies=8, reps=200):
@@ -198,9 +261,13 @@ def bench_decode_fixed(log, copies=8, reps=200):
         binding.mla_decode_fwd(d["q_lat"], d["q_rope"], d["cache"], d["sl"], w["scale"], 32, workspace=d["ws"],
                                o=d["o"], lse=d["lse"])
 
-    for i in range(100):
-        call(i)
-    torch.cuda.synchronize()
+    ctr = [0]
+
+    def rot():
+        call(ctr[0])
+        ctr[0] += 1
+
+    warm(rot, 0.5, min_calls=100)
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i, (a, b) in enumerate(evs):
@@ -227,33 +294,29 @@ def chunk_pairs(Nq, Nk, causal):
     return sum(max(0, min(i + off + 1, Nk)) for i in range(Nq))
 
 
-def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007):
+def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007, cpu=False):
     """bf16 prefill of a chunk of Nq new queries over Nk keys (causal, bottom-right)."""
     import torch
     from mla_latent_kv_attn_amd import binding, workloads
     dev = "cuda:0"
-    q = workloads.attn_inputs(B, H, Nq, D, torch.bfloat16, seed=seed)[0].to(dev)
-    _, k, v = workloads.attn_inputs(B, H, Nk, D, torch.bfloat16, seed=seed + 1)
-    k, v = k.to(dev), v.to(dev)
+    qc = workloads.attn_inputs(B, H, Nq, D, torch.bfloat16, seed=seed)[0]
+    _, kc, vc = workloads.attn_inputs(B, H, Nk, D, torch.bfloat16, seed=seed + 1)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     fn = lambda: binding.attn_fwd_chunk(q, k, v, 1.0 / math.sqrt(D), True, o=o, lse=lse)
-    fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    fn()
-    torch.cuda.synchronize()
-    est = max(time.perf_counter() - t0, 1e-4)
-    for _ in range(max(3, int(0.1 / est))):  # about 0.1 s of warm-up, as for the other prefill lines
-        fn()
-    torch.cuda.synchronize()
-    ms = time_events(fn, max(10, min(100, int(0.2 / est))))
+    ws, wc = warm(fn, 0.5)
+    ms = time_events(fn, max(10, min(100, int(0.2 * wc / ws))))
     avg = sum(ms) / len(ms)
     tf = 4.0 * D * B * H * chunk_pairs(Nq, Nk, True) / (avg * 1e-3) / 1e12
     log(f"prefill chunk bf16 Nq={Nq} Nk={Nk}: {avg:.3f} ms, {tf:.1f} TFLOP/s ({100*tf/BF16_PEAK_TFLOPS:.1f}%)")
-    return {"workload": f"attn_fwd_chunk bf16 B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal=1 (bottom-right)",
+    line = {"workload": f"attn_fwd_chunk bf16 B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal=1 (bottom-right)",
             "ms": round(avg, 4), "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma"}
+    if cpu:
+        del q, k, v, o, lse
+        line["cpu_oracle"] = cpu_prefill_oracle(log, qc, kc, vc, 1.0 / math.sqrt(D), True, "chunk")
+    return line
 
 
 # The decode kernels, their plan layout, and the host code that sets the plan
@@ -261,6 +324,21 @@ def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007):
 DECODE_SOURCES = ("mla_latent_kv_attn_amd/csrc/mla_decode.hip", "mla_latent_kv_attn_amd/csrc/mla_plan.h",
                   "mla_latent_kv_attn_amd/csrc/common.h", "mla_latent_kv_attn_amd/csrc/api.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_varlen_pmc.json")
+
+
+def sources_sha():
+    """SHA-256 over every library source (csrc/* and the C header), in name
+    order; the kernel-stats summaries under profiles/ state the same hash."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "mla_latent_kv_attn_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "mla_attn.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def decode_sources_sha():
@@ -335,11 +413,7 @@ def cpu_baseline(d, log, budget_s=12.0):
         tbytes += L * 1152
         if elapsed >= budget_s:
             break
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores = cpu_threads()
     gbs = tbytes / elapsed / 1e9
     log(f"cpu oracle: {done} sequences, {tbytes/1e6:.1f} MB of cache in {elapsed:.2f} s -> {gbs:.3f} GB/s")
     # The explicit-decompression check on a sample (4 sequences x 128 heads x
@@ -406,10 +480,11 @@ def main():
     copy_gbs = copy_bandwidth(log)
     prefill = {}
     if not args.no_prefill:
-        prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True)
-        prefill["fp32_noncausal"] = bench_prefill(log, "attn_fp32", False, reps=5)
-        prefill["fp32_causal"] = bench_prefill(log, "attn_fp32", True, reps=5)
-        prefill["bf16_chunk"] = bench_prefill_chunk(log)
+        cpu = not args.no_cpu
+        prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True, cpu=cpu)
+        prefill["fp32_noncausal"] = bench_prefill(log, "attn_fp32", False, reps=5, cpu=cpu)
+        prefill["fp32_causal"] = bench_prefill(log, "attn_fp32", True, reps=5, cpu=cpu)
+        prefill["bf16_chunk"] = bench_prefill_chunk(log, cpu=cpu)
     cpu = None if args.no_cpu else cpu_baseline(d, log)
     value = d["kv_bytes"] / (d["ms_step"] * 1e-3) / 1e9
     achieved = d["kv_bytes"] / (d["dec_ms"] * 1e-3) / 1e9
@@ -436,11 +511,13 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(log),
                      "decode_us": round(d["dec_ms"] * 1e3, 2), "decode_us_median": round(d["dec_median"] * 1e3, 2),
                      "decode_us_min": round(d["dec_min"] * 1e3, 2), "absorb_us": round(d["abs_ms"] * 1e3, 2),
+                     "warmup_s": round(d["warm_s"], 2), "warmup_calls": d["warm_calls"],
                      "attainable_copy_GB_s": copy_gbs},
         "value_up_projection": {"workload": "o [256,128,512] @ W_UV [128,512,128] -> [256,128,128] bf16",
                                 "us": round(d["up_ms"] * 1e3, 2),
                                 "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
                                 "note": "timed after the step, not part of value"},
+        "sources_sha256": sources_sha(),
         "cpu_baseline": cpu,
         "decode_fixed": decode_fixed,
         "prefill": prefill,

@@ -32,7 +32,6 @@ Parity status of every public function is stated in its docstring
 
 from .attention import (  # noqa: F401
     attn_ref,
-    attn_probs_ref,
     online_attn_ref,
     causal_kv_tiles,
     is_diagonal_tile,
@@ -46,5 +45,7 @@ from .mla import (  # noqa: F401
     mla_decode_explicit_ref,
     split_partials_ref,
     combine_ref,
+    round_bf16,
+    absorb_decode_ref,
 )
 from .plan import plan_ref, plan_pieces_ref, plan_slot_ref  # noqa: F401

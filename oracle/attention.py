@@ -35,7 +35,6 @@ import numpy as np
 
 __all__ = [
     "attn_ref",
-    "attn_probs_ref",
     "online_attn_ref",
     "causal_kv_tiles",
     "is_diagonal_tile",
@@ -91,21 +90,6 @@ def attn_ref(q, k, v, scale, causal, row_block=256):
                 O[b, h, idx] = (E / l) @ v[b, h]
                 LSE[b, h, idx] = (m + np.log(l))[:, 0]
     return O, LSE
-
-
-def attn_probs_ref(q, k, scale, causal):
-    """The full probability matrix P = softmax(scale Q K^T [masked]), [B,H,N,Nk].
-
-    Small inputs only (it materialises P).  Same definition as ``attn_ref``.
-    """
-    q, k = _f64(q), _f64(k)
-    N, Nk = q.shape[2], k.shape[2]
-    S = scale * np.einsum("bhnd,bhmd->bhnm", q, k)
-    if causal:
-        S = np.where(np.arange(Nk)[None, :] > np.arange(N)[:, None], -np.inf, S)
-    m = S.max(axis=-1, keepdims=True)
-    E = np.exp(S - m)
-    return E / E.sum(axis=-1, keepdims=True)
 
 
 def causal_kv_tiles(q_start, Br, N, Bc, causal):

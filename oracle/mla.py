@@ -41,7 +41,12 @@ through explicit decompression versus the absorbed decode, split invariance of
 the combine over arbitrary split plans, combine closed forms; for the value
 up-projection, attention over explicitly decompressed values versus the
 latent output projected afterwards, a selection matrix (exact copy of chosen
-latent dims), and pure-Python loops on tiny inputs.
+latent dims), and pure-Python loops on tiny inputs; for the bfloat16
+rounding, torch's float32 -> bfloat16 conversion (a single rounding for
+float32-representable values), hand-made ties that must go to the even
+neighbour, and the set of representable values being fixed points; the
+end-to-end reference is its two pinned parts composed, checked once more
+against explicit key decompression on a bf16-rounded query.
 """
 
 import numpy as np
@@ -58,6 +63,8 @@ __all__ = [
     "up_project_v_ref",
     "decompress_v_ref",
     "mla_decode_values_explicit_ref",
+    "round_bf16",
+    "absorb_decode_ref",
 ]
 
 LATENT_DIM = 512
@@ -116,6 +123,39 @@ def absorb_ref(q_nope, w_uk):
     for h in range(H):
         out[:, h, :] = q_nope[:, h, :] @ w_uk[h]
     return out
+
+
+def round_bf16(x):
+    """Round float64 values to bfloat16 (1-8-7), round to nearest, ties to even.
+
+    bfloat16 keeps 8 significant bits.  For x = m 2^e with 0.5 <= |m| < 1
+    (numpy's frexp), the spacing of bfloat16 values around x is 2^(e-8),
+    never finer than 2^-133 (the subnormal spacing below the smallest
+    normal, 2^-126).  x / spacing is exact in float64, np.rint rounds it to
+    the nearest integer with ties to even, and the product is exact again.
+    Values beyond the largest finite bfloat16 are not expected here and are
+    not clamped.  Returns float64 arrays holding bfloat16 values.
+    (The precision the decode's query is stored in after absorption:
+    q_lat is kept in bf16 before the decode.)
+    """
+    x = _f64(x)
+    _, e = np.frexp(x)
+    spacing = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.rint(x / spacing) * spacing
+
+
+def absorb_decode_ref(q_nope, w_uk, q_rope, cache, seqlens, scale):
+    """The decode step end to end from the un-absorbed query.
+
+    q_lat = round_bf16(absorb_ref(q_nope, W_UK)) -- the absorption in float64,
+    then the one rounding to bfloat16 that storing q_lat implies -- followed
+    by ``mla_decode_ref`` on [q_lat || q_rope] against the cache.
+    Returns (O [B, H, 512], LSE [B, H]).
+    ([MLA-FA3 article] section 2: absorb W_UK into the query once, then take
+    the 576-wide dot products against the cache as stored.)
+    """
+    q_lat = round_bf16(absorb_ref(q_nope, w_uk))
+    return mla_decode_ref(q_lat, q_rope, cache, seqlens, scale)
 
 
 def decompress_k_ref(c_latent, w_uk):

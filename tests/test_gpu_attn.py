@@ -49,6 +49,31 @@ def test_fp32_causal_row0_is_v0_bitwise():
     assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
 
 
+def test_fp32_identical_keys_give_mean_of_v():
+    q, k, v = workloads.attn_inputs(1, 2, 300, 64, torch.float32, seed=81)
+    k = k[:, :, :1].expand(-1, -1, 300, -1).contiguous()
+    o, l = run(q, k, v, 0.125, False)
+    ref = np64(v).mean(axis=2, keepdims=True).repeat(300, axis=2)
+    check_f32(o, ref, "O=mean(V)")
+    s = 0.125 * np.einsum("bhnd,bhd->bhn", np64(q), np64(k[:, :, 0]))
+    check_lse(l, s + math.log(300), "LSE=s+ln N")
+    oc, lc = run(q, k, v, 0.125, True)
+    refc = np.cumsum(np64(v), axis=2) / np.arange(1, 301)[None, None, :, None]
+    check_f32(oc, refc, "causal O=prefix mean(V)")
+    check_lse(lc, s + np.log(np.arange(1, 301))[None, None, :], "causal LSE=s+ln(i+1)")
+
+
+def whole_slices_ref(q, k, v, scale, causal, slices):
+    """Oracle O and LSE of whole (b, h) slices, every query row."""
+    O, L = [], []
+    for b, h in slices:
+        o, l = OA.attn_ref(np64(q[b:b + 1, h:h + 1]), np64(k[b:b + 1, h:h + 1]), np64(v[b:b + 1, h:h + 1]),
+                           scale, causal)
+        O.append(o[0, 0])
+        L.append(l[0, 0])
+    return np.stack(O), np.stack(L)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp32_full_size_sampled(causal):
     w = workloads.attn_workload("attn_fp32")
@@ -61,6 +86,12 @@ def test_fp32_full_size_sampled(causal):
     check_f32(og, Or, "O(sampled)")
     check_lse(lg, Lr, "LSE(sampled)")
     assert torch.isfinite(o).all()
+    # two whole (b, h) slices: every query tile, and under the causal mask
+    # every rank of the heaviest-first order
+    sl = [(0, 0), (3, 7)]
+    Or, Lr = whole_slices_ref(w["q"], w["k"], w["v"], w["scale"], causal, sl)
+    check_f32(torch.stack([o[b, h] for b, h in sl]), Or, "O(whole slices)")
+    check_lse(torch.stack([l[b, h] for b, h in sl]), Lr, "LSE(whole slices)")
 
 
 # ----------------------------------------------------------------- bf16 ----
@@ -105,6 +136,10 @@ def test_bf16_full_size_sampled_and_deterministic():
     check_bf16(og, Or, "O(sampled)")
     check_lse(lg, Lr, "LSE(sampled)")
     assert torch.isfinite(o1.float()).all()
+    sl = [(0, 0), (1, 9), (3, 15)]
+    Or, Lr = whole_slices_ref(w["q"], w["k"], w["v"], w["scale"], True, sl)
+    check_bf16(torch.stack([o1[b, h] for b, h in sl]), Or, "O(whole slices)")
+    check_lse(torch.stack([l1[b, h] for b, h in sl]), Lr, "LSE(whole slices)")
 
 
 def test_bf16_noncausal_full_size_sampled():
@@ -115,6 +150,10 @@ def test_bf16_noncausal_full_size_sampled():
     Or, Lr = attn_rows_ref(w["q"], w["k"], w["v"], w["scale"], False, picks)
     check_bf16(torch.stack([o[b, h, i] for b, h, i in picks]), Or, "O(sampled)")
     check_lse(torch.stack([l[b, h, i] for b, h, i in picks]), Lr, "LSE(sampled)")
+    sl = [(2, 3), (3, 12)]
+    Or, Lr = whole_slices_ref(w["q"], w["k"], w["v"], w["scale"], False, sl)
+    check_bf16(torch.stack([o[b, h] for b, h in sl]), Or, "O(whole slices)")
+    check_lse(torch.stack([l[b, h] for b, h in sl]), Lr, "LSE(whole slices)")
 
 
 def test_lse_optional_and_outputs_untouched_on_error():
@@ -165,3 +204,19 @@ def test_bf16_chunk(Nq, Nk, causal):
     Or, Lr = OA.attn_ref(np64(q), np64(k), np64(v), sc, causal)
     check_bf16(o, Or, "O")
     check_lse(l, Lr, "LSE")
+
+
+def test_bf16_chunk_at_benchmark_shape():
+    # The chunk shape the benchmark times: B=4 H=16, 1024 queries over 4096
+    # keys, causal bottom-right; whole (b, h) slices (every query tile).
+    B, H, Nq, Nk, D = 4, 16, 1024, 4096, 128
+    say(f"bf16 chunk at the benchmark shape B={B} H={H} Nq={Nq} Nk={Nk}")
+    q, k, v = chunk_inputs(B, H, Nq, Nk, D, torch.bfloat16, 1007)
+    sc = 1 / math.sqrt(D)
+    o, l = binding.attn_fwd_chunk(q.to(DEV), k.to(DEV), v.to(DEV), sc, True)
+    sync()
+    sl = [(0, 0), (1, 5), (2, 10), (3, 15)]
+    Or, Lr = whole_slices_ref(q, k, v, sc, True, sl)
+    check_bf16(torch.stack([o[b, h] for b, h in sl]), Or, "O(whole slices)")
+    check_lse(torch.stack([l[b, h] for b, h in sl]), Lr, "LSE(whole slices)")
+    assert torch.isfinite(o.float()).all()

@@ -65,14 +65,35 @@ def test_against_torch_sdpa_fp64(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_rows_of_P_sum_to_one_and_mask(causal):
-    q, k = rnd((2, 2, 9, 5), 7), rnd((2, 2, 9, 5), 8)
-    P = A.attn_probs_ref(q, k, 0.5, causal)
-    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
-    if causal:
-        assert np.all(P[..., np.triu_indices(9, 1)[0], np.triu_indices(9, 1)[1]] == 0.0)
-        # row 0 puts all its mass on key 0
-        assert np.all(P[..., 0, 0] == 1.0)
+@pytest.mark.parametrize("Nq,Nk", [(9, 9), (4, 9), (9, 4)])
+def test_rows_of_P_sum_to_one_and_mask(causal, Nq, Nk):
+    # With V = I (Dv = Nk) attn_ref returns P itself; with V = ones, the row
+    # sums.  P is checked against scalar softmax loops, its rows must sum to
+    # one, and the causal zero pattern is the bottom-right one.
+    q, k = rnd((2, 2, Nq, 5), 7), rnd((2, 2, Nk, 5), 8)
+    eye = np.broadcast_to(np.eye(Nk), (2, 2, Nk, Nk))
+    P, _ = A.attn_ref(q, k, eye, 0.5, causal)
+    off = Nk - Nq
+    for b in range(2):
+        for h in range(2):
+            for i in range(Nq):
+                lim = min(i + off + 1, Nk) if causal else Nk
+                if lim <= 0:
+                    assert np.all(P[b, h, i] == 0.0)
+                    continue
+                s = [0.5 * math.fsum(q[b, h, i, d] * k[b, h, j, d] for d in range(5)) for j in range(lim)]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = math.fsum(e)
+                np.testing.assert_allclose(P[b, h, i, :lim], [x / tot for x in e], rtol=0, atol=1e-14)
+                assert np.all(P[b, h, i, lim:] == 0.0)
+    seen = np.array([min(i + off + 1, Nk) > 0 if causal else Nk > 0 for i in range(Nq)])
+    np.testing.assert_allclose(P.sum(-1)[..., seen], 1.0, rtol=0, atol=1e-12)
+    ones = np.ones((2, 2, Nk, 3))
+    R, _ = A.attn_ref(q, k, ones, 0.5, causal)
+    np.testing.assert_allclose(R[..., seen, :], 1.0, rtol=0, atol=1e-12)
+    if causal and Nq == Nk:
+        assert np.all(P[..., 0, 0] == 1.0)  # row 0 puts all its mass on key 0
 
 
 def test_causal_row0_is_v0_exactly():

@@ -209,3 +209,53 @@ def test_up_projection_brute_force_tiny():
             for d in range(Dv):
                 ref = math.fsum(float(o[b, h, c]) * float(w[h, c, d]) for c in range(Dl))
                 assert abs(got[b, h, d] - ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding and the end-to-end (absorb -> round -> decode) reference
+# ---------------------------------------------------------------------------
+def test_round_bf16_matches_torch_on_float32_values():
+    # For float32-representable inputs torch's float32 -> bfloat16 conversion
+    # is one round-to-nearest-even, the same operation.
+    x = np.concatenate([rnd((20000,), 80), rnd((2000,), 81, 1e-30), rnd((2000,), 82, 1e30),
+                        rnd((500,), 83, 1e-39)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = M.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_bf16_ties_go_to_even():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (even: 1); 1 + 3*2^-8 lies
+    # halfway between 1 + 2^-7 (odd mantissa) and 1 + 2^-6 (even).
+    assert M.round_bf16(1 + 2.0 ** -8) == 1.0
+    assert M.round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert M.round_bf16(-(1 + 3 * 2.0 ** -8)) == -(1 + 2.0 ** -6)
+    assert M.round_bf16(1 + 2.0 ** -8 + 2.0 ** -30) == 1 + 2.0 ** -7   # just above the tie
+    assert M.round_bf16(0.0) == 0.0
+    # bfloat16 values are fixed points
+    v = np.array([1.0, -3.5, 2.0 ** -126, 2.0 ** -133, 1.9921875 * 2.0 ** 100])
+    np.testing.assert_array_equal(M.round_bf16(v), v)
+
+
+def test_absorb_decode_ref_composition_and_explicit_path():
+    B, H, Dn, S = 2, 3, 128, 10
+    q_nope, w_uk = rnd((B, H, Dn), 84), rnd((H, Dn, 512), 85, 0.02)
+    q_rope, cache = rnd((B, H, 64), 86), rnd((B, S, 576), 87)
+    lens = [10, 4]
+    scale = 1 / math.sqrt(576)
+    O, L = M.absorb_decode_ref(q_nope, w_uk, q_rope, cache, lens, scale)
+    ql = M.absorb_ref(q_nope, w_uk)
+    qlr = torch.from_numpy(ql.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    # the rounding matters: the unrounded query gives visibly different scores
+    assert np.abs(qlr - ql).max() > 1e-5
+    Or, Lr = M.mla_decode_ref(qlr, q_rope, cache, lens, scale)
+    # torch rounds via float32 (two roundings); a double rounding can only
+    # differ from the single one on near-ties, which these draws do not hit.
+    np.testing.assert_allclose(O, Or, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L, Lr, rtol=0, atol=1e-13)
+    # and against scores taken through explicitly decompressed keys with the
+    # rounding error of q_lat moved into q_nope's side: both are within the
+    # score perturbation that the bf16 rounding of q_lat causes
+    Oe, Le = M.mla_decode_explicit_ref(q_nope, q_rope, w_uk, cache, lens, scale)
+    ds = scale * np.abs(qlr - ql).max() * np.abs(cache[..., :512]).sum(-1).max()
+    assert np.abs(L - Le).max() <= ds
