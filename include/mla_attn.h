@@ -25,7 +25,8 @@
  *   - MLA_ERR_HIP is returned when the HIP runtime reports an error while
  *     enqueueing (for example when no GPU is present).
  *   - Nothing throws across this interface.  The library keeps no state
- *     except a per-device cache of the compute-unit count.
+ *     except a per-device cache of the compute-unit count and, for
+ *     mla_decode_fwd_noalloc only, a fixed per-device scratch array.
  */
 #ifndef MLA_ATTN_H
 #define MLA_ATTN_H
@@ -45,7 +46,9 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 3, /* valid but not compiled (see per-function list) */
     MLA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
     MLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
-    MLA_ERR_HIP = 6          /* the HIP runtime reported an error              */
+    MLA_ERR_HIP = 6,         /* the HIP runtime reported an error              */
+    MLA_ERR_SCRATCH = 7      /* mla_decode_fwd_noalloc: the call needs more
+                                than the fixed scratch                         */
 } mla_status_t;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
@@ -134,6 +137,31 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* q_rope, const void* k
                             const int* seqlens, void* o, float* lse,
                             int B, int H, int S_max, float scale, int num_splits,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_decode_fwd_noalloc - mla_decode_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same inputs, outputs, layouts, results (bitwise) and errors as
+ * mla_decode_fwd, whose kernels it runs.  The workspace is a fixed device
+ * array inside the library, MLA_DECODE_NOALLOC_SCRATCH_BYTES (72 MiB) per
+ * device, allocated when the library's code is loaded on that device and
+ * held until the process ends; this call allocates and frees nothing
+ * itself.  A shape whose workspace (mla_decode_workspace_size) exceeds it
+ * returns MLA_ERR_SCRATCH and enqueues nothing; H = 128 fits up to 256
+ * split-kernel parts (any B on a 256-CU device with num_splits >= 2, and
+ * every B with num_splits = 1).  Nothing in the scratch needs to start at
+ * zero: every call writes what it reads.
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap in time on one device (several streams, several host threads)
+ * race and give undefined results; order them on one stream.
+ */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* q_rope, const void* kv_cache,
+                                    const int* seqlens, void* o, float* lse,
+                                    int B, int H, int S_max, float scale, int num_splits,
+                                    hipStream_t stream);
 
 /*
  * mla_combine - log-sum-exp merge of split-KV partials ([MLA-FA3 article],

@@ -13,6 +13,7 @@ __all__ = [
     "attn_fwd_chunk",
     "mla_decode_fwd",
     "mla_decode_workspace_size",
+    "mla_decode_fwd_noalloc",
     "mla_combine",
     "mla_absorb_q",
     "mla_up_proj_v",

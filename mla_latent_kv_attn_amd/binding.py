@@ -15,12 +15,12 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_attn.so")
 _lib = None
 
-MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(7)
+(MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP,
+ MLA_ERR_SCRATCH) = range(8)
 MLA_F32, MLA_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_chunk", "mla_decode_workspace_size", "mla_decode_fwd", "mla_combine", "mla_absorb_q",
-            "mla_up_proj_v",
-            "mla_status_string")
+EXPORTED = ("attn_fwd", "attn_fwd_chunk", "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_fwd_noalloc",
+            "mla_combine", "mla_absorb_q", "mla_up_proj_v", "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -50,6 +50,8 @@ def load(path=None):
     lib.mla_decode_workspace_size.restype = sz
     lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, vp, sz, vp]
     lib.mla_decode_fwd.restype = i
+    lib.mla_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, vp]
+    lib.mla_decode_fwd_noalloc.restype = i
     lib.mla_combine.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.mla_combine.restype = i
     lib.mla_absorb_q.argtypes = [vp, vp, vp, i, i, i, i, vp]
@@ -171,6 +173,27 @@ def mla_decode_fwd(q_lat, q_rope, kv_cache, seqlens, scale, num_splits, workspac
                                B, H, S_max, float(scale), int(num_splits), _ptr(workspace),
                                workspace.numel(), _stream(q_lat.device))
     _check("mla_decode_fwd", st)
+    return o, lse
+
+
+def mla_decode_fwd_noalloc(q_lat, q_rope, kv_cache, seqlens, scale, num_splits, o=None, lse=None):
+    """mla_decode_fwd with the library's fixed device scratch as workspace
+    (no workspace argument; calls on one device must not overlap)."""
+    B, H, _ = q_lat.shape
+    S_max = kv_cache.shape[1]
+    _need(q_lat, "q_lat", torch.bfloat16, (B, H, 512))
+    _need(q_rope, "q_rope", torch.bfloat16, (B, H, 64))
+    _need(kv_cache, "kv_cache", torch.bfloat16, (B, S_max, 576))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if o is None:
+        o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q_lat.device)
+    _need(o, "o", torch.bfloat16, (B, H, 512))
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_lat.device)
+    _need(lse, "lse", torch.float32, (B, H))
+    st = load().mla_decode_fwd_noalloc(_ptr(q_lat), _ptr(q_rope), _ptr(kv_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
+                                       B, H, S_max, float(scale), int(num_splits), _stream(q_lat.device))
+    _check("mla_decode_fwd_noalloc", st)
     return o, lse
 
 

@@ -22,6 +22,7 @@ hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* 
 hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __bf16* cache, const int* seqlens,
                              __bf16* o, float* lse, int B, int H, int S_max, float scale, int num_splits,
                              const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream);
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_mla_combine(const float* o_part, const float* lse_part, __bf16* o, float* lse, int B, int H,
                               int S, hipStream_t stream);
 hipError_t launch_mla_absorb(const __bf16* q_nope, const __bf16* w_uk, __bf16* q_lat, int B, int H, int Dn, int Dl,
@@ -96,6 +97,8 @@ MLA_EXPORT const char* mla_status_string(mla_status_t s) {
         case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: a pointer is not 16-byte aligned";
         case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
         case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error";
+        case MLA_ERR_SCRATCH:
+            return "MLA_ERR_SCRATCH: the call needs more workspace than the library's fixed 72 MiB scratch";
     }
     return "unknown mla_status_t";
 }
@@ -171,6 +174,27 @@ MLA_EXPORT mla_status_t mla_decode_fwd(const void* q_lat, const void* q_rope, co
     return hip_status(mla::launch_mla_decode(
         static_cast<const __bf16*>(q_lat), static_cast<const __bf16*>(q_rope), static_cast<const __bf16*>(kv_cache),
         seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, workspace, stream));
+}
+
+MLA_EXPORT mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* q_rope, const void* kv_cache,
+                                               const int* seqlens, void* o, float* lse, int B, int H, int S_max,
+                                               float scale, int num_splits, hipStream_t stream) {
+    if (!q_lat || !q_rope || !kv_cache || !seqlens || !o) return MLA_ERR_NULL;
+    if (!decode_shape_ok(B, H, num_splits) || S_max < 1 || !good_scale(scale)) return MLA_ERR_SHAPE;
+    if ((long long)B * S_max > (long long)INT_MAX / mla::kRow) return MLA_ERR_SHAPE;
+    if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(seqlens) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return MLA_ERR_ALIGN;
+    const int cus = current_cu_count();
+    if (cus <= 0) return MLA_ERR_HIP;
+    const DecodeConfig c = decode_config(B, num_splits, cus);
+    const mla::PlanLayout L = mla::plan_layout(B, H, c.parts, c.slots);
+    if (L.total_bytes > mla::kNoAllocScratchBytes) return MLA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (mla::noalloc_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+    return hip_status(mla::launch_mla_decode(
+        static_cast<const __bf16*>(q_lat), static_cast<const __bf16*>(q_rope), static_cast<const __bf16*>(kv_cache),
+        seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, ws, stream));
 }
 
 MLA_EXPORT mla_status_t mla_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B, int H,

@@ -40,6 +40,7 @@
 // MFMA-to-MFMA accumulator chains; the places where ordinary instructions
 // read MFMA results carry explicit wait states (s_nop).
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "mla_plan.h"
@@ -945,6 +946,35 @@ hipError_t ensure_smem_attr(const void* fn, int bytes) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(bytes, std::memory_order_release);
     return e;
+}
+
+// Workspace of mla_decode_fwd_noalloc: one file-scope device array, so that
+// that entry point needs no allocation.  Every device the library runs on
+// holds its own copy until the process ends.  In host code `scratch` only
+// names the symbol; its device address (per device) comes from
+// hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    static std::atomic<void*> addr[64];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 static PlanArgs plan_args(const PlanLayout& L) {

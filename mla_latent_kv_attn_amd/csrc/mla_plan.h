@@ -19,6 +19,8 @@ constexpr int kRow = kLatent + kRope;  // 576 bf16 per cached token
 constexpr int kMaxSplits = 32;
 constexpr int kMaxBatch = 1 << 16;
 constexpr int kPlanMaxParts = 1024;  // split-kernel parts in line mode (one per CU, capped)
+// Fixed device scratch of mla_decode_fwd_noalloc (72 MiB per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)72 << 20;
 
 // Header words (int32) at the start of the workspace.
 enum PlanWord {

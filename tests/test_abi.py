@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         txt = lib.mla_status_string(s).decode()
         assert txt.startswith("MLA_"), txt
     assert lib.mla_status_string(99).decode() == "unknown mla_status_t"
@@ -141,3 +141,17 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert _attn(lib) == binding.MLA_ERR_HIP
     assert _dec(lib) == binding.MLA_ERR_HIP
     assert lib.mla_decode_workspace_size(4, 128, 4) == 0
+
+
+def test_decode_noalloc_validation_codes(lib):
+    def call(ql=P, qr=P, c=P, sl=P, o=P, lse=P, B=2, H=128, S=64, scale=0.04, ns=4):
+        return lib.mla_decode_fwd_noalloc(ql, qr, c, sl, o, lse, B, H, S, scale, ns, None)
+    assert call(ql=None) == binding.MLA_ERR_NULL
+    assert call(sl=None) == binding.MLA_ERR_NULL
+    assert call(B=0) == binding.MLA_ERR_SHAPE
+    assert call(H=24) == binding.MLA_ERR_SHAPE
+    assert call(ns=33) == binding.MLA_ERR_SHAPE
+    assert call(S=0) == binding.MLA_ERR_SHAPE
+    assert call(scale=-1.0) == binding.MLA_ERR_SHAPE
+    assert call(c=BAD) == binding.MLA_ERR_ALIGN
+    assert call(lse=BAD) == binding.MLA_ERR_ALIGN
