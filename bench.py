@@ -154,24 +154,31 @@ def bench_decode(args, log):
         f"parts_used={plan['parts_used']} t={plan['t']} max_nsplit={max(plan['nsplit'])}")
     absorb_bytes = (q_nope.numel() + w_uk.numel() + q_lat.numel()) * 2
     # The value up-projection (o_v = o W_UV[h], 512 -> 128) is the step after
-    # the decode; it is timed on its own, outside the step.
+    # the decode; it is timed outside the step, on its own and fused with the
+    # decode's merge (mla_decode_fwd_v).
     w_uv = workloads.w_uv_weights(H=H).to(dev)
     o_v = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
-    for _ in range(10):
-        binding.mla_up_proj_v(o, w_uv, o_v=o_v)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(st)
-    for _ in range(50):
-        binding.mla_up_proj_v(o, w_uv, o_v=o_v)
-    b.record(st)
-    b.synchronize()
-    up_ms = a.elapsed_time(b) / 50
+    ws_v = binding.alloc_decode_v_workspace(B, H, ns, dev)
+    up = lambda: binding.mla_up_proj_v(o, w_uv, o_v=o_v)
+    dec_v = lambda: binding.mla_decode_fwd_v(q_lat, q_rope, cache, sl, w_uv, w["scale"], ns, workspace=ws_v,
+                                             o_v=o_v, lse=lse)
+
+    def unfused():
+        decode()
+        up()
+
+    warm(dec_v, 0.3)
+    warm(unfused, 0.3)
+    up_ms = sorted(time_events(up, 50))[25]
+    dv_ms = sorted(time_events(dec_v, 50))[25]
+    uf_ms = sorted(time_events(unfused, 50))[25]
     up_bytes = (o.numel() + w_uv.numel() + o_v.numel()) * 2
-    log(f"value up-projection: {up_ms*1e3:.1f} us ({up_bytes/(up_ms*1e-3)/1e9:.0f} GB/s)")
+    log(f"value up-projection: {up_ms*1e3:.1f} us ({up_bytes/(up_ms*1e-3)/1e9:.0f} GB/s); decode + W_UV fused "
+        f"{dv_ms*1e3:.1f} us, unfused {uf_ms*1e3:.1f} us (medians)")
     dec_sorted = sorted(dec_ms)
     return dict(workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
                 dec_median=dec_sorted[len(dec_sorted) // 2], dec_min=dec_sorted[0],
-                absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes,
+                absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes, dv_ms=dv_ms, uf_ms=uf_ms,
                 warm_s=warm_s, warm_calls=warm_calls)
 
 
@@ -516,7 +523,11 @@ def main():
         "value_up_projection": {"workload": "o [256,128,512] @ W_UV [128,512,128] -> [256,128,128] bf16",
                                 "us": round(d["up_ms"] * 1e3, 2),
                                 "GB_s": round(d["up_bytes"] / (d["up_ms"] * 1e-3) / 1e9, 1),
-                                "note": "timed after the step, not part of value"},
+                                "decode_v_fused_us": round(d["dv_ms"] * 1e3, 2),
+                                "decode_then_up_proj_us": round(d["uf_ms"] * 1e3, 2),
+                                "fused_GB_s": round(d["kv_bytes"] / (d["dv_ms"] * 1e-3) / 1e9, 1),
+                                "note": "timed after the step (medians), not part of value; fused = "
+                                        "mla_decode_fwd_v (merge + W_UV in one kernel)"},
         "sources_sha256": sources_sha(),
         "cpu_baseline": cpu,
         "decode_fixed": decode_fixed,

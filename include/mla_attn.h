@@ -139,6 +139,44 @@ mla_status_t mla_decode_fwd(const void* q_lat, const void* q_rope, const void* k
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_decode_v_workspace_size - bytes of device workspace mla_decode_fwd_v
+ * needs for (B, H, num_splits) on the CURRENT device; 0 if the arguments are
+ * invalid or the device cannot be queried.  At least
+ * mla_decode_workspace_size(B, H, num_splits): every sequence keeps its
+ * latent partials (B * H * 1 KiB and up).
+ */
+size_t mla_decode_v_workspace_size(int B, int H, int num_splits);
+
+/*
+ * mla_decode_fwd_v - the absorbed MLA decode followed by the value
+ * up-projection, with the split merge fused into the projection
+ * ([MLA-FA3 article] fused dataflow figure: W_UK and W_UV belong to the
+ * in-place absorption stage; the online-softmax partial reduction precedes
+ * the output).
+ *   o_lat[b, h] = the latent output of mla_decode_fwd (merged in fp32,
+ *                 rounded to bf16, never written to memory)
+ *   o_v[b, h, :] = o_lat[b, h, :] @ W_UV[h]    (fp32 accumulation)
+ *   lse[b, h]   = as mla_decode_fwd
+ * Attention is linear in its values, so o_v equals attention over the
+ * explicitly decompressed values c^KV W_UV[h] without forming them.  The
+ * results are bitwise those of mla_decode_fwd followed by mla_up_proj_v.
+ * Two kernels are enqueued (the split kernel, with the plan inside it or a
+ * plan kernel before it, then the merge + up-projection).
+ *
+ * q_lat, q_rope, kv_cache, seqlens, B, H, S_max, scale, num_splits: as
+ *            mla_decode_fwd.
+ * w_uv     : [H, 512, Dv] bf16 (per head: latent dim x value dim)
+ * o_v      : [B, H, Dv] bf16 (round to nearest even); a length of 0 gives 0.
+ * lse      : [B, H] f32 (may be NULL to skip it)
+ * Dv       : multiple of 128, at most 4096 (else MLA_ERR_UNSUPPORTED).
+ * workspace: at least mla_decode_v_workspace_size(B, H, num_splits) bytes.
+ */
+mla_status_t mla_decode_fwd_v(const void* q_lat, const void* q_rope, const void* kv_cache,
+                              const int* seqlens, const void* w_uv, void* o_v, float* lse,
+                              int B, int H, int S_max, int Dv, float scale, int num_splits,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mla_decode_fwd_noalloc - mla_decode_fwd without a workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.

@@ -14,6 +14,8 @@ __all__ = [
     "mla_decode_fwd",
     "mla_decode_workspace_size",
     "mla_decode_fwd_noalloc",
+    "mla_decode_v_workspace_size",
+    "mla_decode_fwd_v",
     "mla_combine",
     "mla_absorb_q",
     "mla_up_proj_v",

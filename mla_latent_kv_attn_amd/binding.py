@@ -20,7 +20,8 @@ _lib = None
 MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_chunk", "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_fwd_noalloc",
-            "mla_combine", "mla_absorb_q", "mla_up_proj_v", "mla_status_string")
+            "mla_decode_v_workspace_size", "mla_decode_fwd_v", "mla_combine", "mla_absorb_q", "mla_up_proj_v",
+            "mla_status_string")
 
 
 class MlaError(RuntimeError):
@@ -50,6 +51,10 @@ def load(path=None):
     lib.mla_decode_workspace_size.restype = sz
     lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, vp, sz, vp]
     lib.mla_decode_fwd.restype = i
+    lib.mla_decode_v_workspace_size.argtypes = [i, i, i]
+    lib.mla_decode_v_workspace_size.restype = sz
+    lib.mla_decode_fwd_v.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.mla_decode_fwd_v.restype = i
     lib.mla_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, vp]
     lib.mla_decode_fwd_noalloc.restype = i
     lib.mla_combine.argtypes = [vp, vp, vp, vp, i, i, i, vp]
@@ -174,6 +179,44 @@ def mla_decode_fwd(q_lat, q_rope, kv_cache, seqlens, scale, num_splits, workspac
                                workspace.numel(), _stream(q_lat.device))
     _check("mla_decode_fwd", st)
     return o, lse
+
+
+def mla_decode_v_workspace_size(B, H, num_splits):
+    return int(load().mla_decode_v_workspace_size(int(B), int(H), int(num_splits)))
+
+
+def alloc_decode_v_workspace(B, H, num_splits, device):
+    n = mla_decode_v_workspace_size(B, H, num_splits)
+    if n == 0:
+        raise MlaError("mla_decode_v_workspace_size", MLA_ERR_SHAPE)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mla_decode_fwd_v(q_lat, q_rope, kv_cache, seqlens, w_uv, scale, num_splits, workspace=None, o_v=None, lse=None):
+    """Decode + value up-projection. w_uv [H,512,Dv] bf16.
+    Returns (o_v [B,H,Dv] bf16, lse [B,H] fp32)."""
+    B, H, _ = q_lat.shape
+    S_max = kv_cache.shape[1]
+    Dv = w_uv.shape[2]
+    _need(q_lat, "q_lat", torch.bfloat16, (B, H, 512))
+    _need(q_rope, "q_rope", torch.bfloat16, (B, H, 64))
+    _need(kv_cache, "kv_cache", torch.bfloat16, (B, S_max, 576))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, 512, Dv))
+    if workspace is None:
+        workspace = alloc_decode_v_workspace(B, H, num_splits, q_lat.device)
+    _need(workspace, "workspace", torch.uint8)
+    if o_v is None:
+        o_v = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q_lat.device)
+    _need(o_v, "o_v", torch.bfloat16, (B, H, Dv))
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_lat.device)
+    _need(lse, "lse", torch.float32, (B, H))
+    st = load().mla_decode_fwd_v(_ptr(q_lat), _ptr(q_rope), _ptr(kv_cache), _ptr(seqlens), _ptr(w_uv), _ptr(o_v),
+                                 _ptr(lse), B, H, S_max, Dv, float(scale), int(num_splits), _ptr(workspace),
+                                 workspace.numel(), _stream(q_lat.device))
+    _check("mla_decode_fwd_v", st)
+    return o_v, lse
 
 
 def mla_decode_fwd_noalloc(q_lat, q_rope, kv_cache, seqlens, scale, num_splits, o=None, lse=None):

@@ -21,7 +21,8 @@ hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* 
                                 int H, int Nq, int Nk, float scale, bool causal, hipStream_t stream);
 hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __bf16* cache, const int* seqlens,
                              __bf16* o, float* lse, int B, int H, int S_max, float scale, int num_splits,
-                             const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream);
+                             const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream,
+                             const __bf16* w_uv, int Dv);
 hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_mla_combine(const float* o_part, const float* lse_part, __bf16* o, float* lse, int B, int H,
                               int S, hipStream_t stream);
@@ -51,21 +52,23 @@ inline bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 // Launch configuration of the split-KV decode.  Parts = one workgroup per
 // compute unit on the cost line (at most B * num_splits); one per sequence
-// when num_splits == 1.  c0 charges each sequence the fixed cost of a piece:
-// loading its query block, filling and draining the tile pipeline, and
-// writing its output.  Timestamps per workgroup on MI355X (256 sequences of
-// 256..8192 tokens) put that cost at about 15 us, against about 1.9 us per
-// 32-token step, i.e. four 64-token tiles; c0 = 4 measured fastest among
-// 3, 4, 5 and 6 (308.6 us per call against 312.2 us for 6).  t_min keeps
-// parts from becoming so short that the fixed cost dominates.
+// when num_splits == 1.  c0 charges each sequence the fixed cost of a piece
+// (loading its query block, filling and draining the tile pipeline, writing
+// its output), in 32-token plan tiles.  Timestamps per workgroup on MI355X
+// (256 sequences of 256..8192 tokens) put that cost at about 15 us, against
+// about 1.9 us per 32-token step; c0 = 8 (256 tokens) measured fastest in a
+// sweep of 6..12 tokens-equivalent (308.6 us per call against 312.2 us for
+// 12).  t_min keeps parts from becoming so short that the fixed cost
+// dominates.
 struct DecodeConfig {
     int parts, slots, c0, t_min;
 };
 
-DecodeConfig decode_config(int B, int num_splits, int cus) {
+// vmode (mla_decode_fwd_v): every piece keeps a partial slot, b + p.
+DecodeConfig decode_config(int B, int num_splits, int cus, bool vmode = false) {
     DecodeConfig c;
-    c.c0 = 4;
-    c.t_min = 4;
+    c.c0 = 8;
+    c.t_min = 8;
     if (num_splits == 1) {
         c.parts = B;
         c.slots = 0;
@@ -76,6 +79,7 @@ DecodeConfig decode_config(int B, int num_splits, int cus) {
         c.parts = (int)p;
         c.slots = 2 * c.parts;
     }
+    if (vmode) c.slots = B + c.parts;
     return c;
 }
 
@@ -173,7 +177,7 @@ MLA_EXPORT mla_status_t mla_decode_fwd(const void* q_lat, const void* q_rope, co
     if (workspace_bytes < L.total_bytes) return MLA_ERR_WORKSPACE;
     return hip_status(mla::launch_mla_decode(
         static_cast<const __bf16*>(q_lat), static_cast<const __bf16*>(q_rope), static_cast<const __bf16*>(kv_cache),
-        seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, workspace, stream));
+        seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, workspace, stream, nullptr, 0));
 }
 
 MLA_EXPORT mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* q_rope, const void* kv_cache,
@@ -194,7 +198,38 @@ MLA_EXPORT mla_status_t mla_decode_fwd_noalloc(const void* q_lat, const void* q_
     if (mla::noalloc_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
     return hip_status(mla::launch_mla_decode(
         static_cast<const __bf16*>(q_lat), static_cast<const __bf16*>(q_rope), static_cast<const __bf16*>(kv_cache),
-        seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, ws, stream));
+        seqlens, static_cast<__bf16*>(o), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, ws, stream, nullptr, 0));
+}
+
+MLA_EXPORT size_t mla_decode_v_workspace_size(int B, int H, int num_splits) {
+    if (!decode_shape_ok(B, H, num_splits)) return 0;
+    const int cus = current_cu_count();
+    if (cus <= 0) return 0;
+    const DecodeConfig c = decode_config(B, num_splits, cus, true);
+    return mla::plan_layout(B, H, c.parts, c.slots).total_bytes;
+}
+
+MLA_EXPORT mla_status_t mla_decode_fwd_v(const void* q_lat, const void* q_rope, const void* kv_cache,
+                                         const int* seqlens, const void* w_uv, void* o_v, float* lse, int B, int H,
+                                         int S_max, int Dv, float scale, int num_splits, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    if (!q_lat || !q_rope || !kv_cache || !seqlens || !w_uv || !o_v) return MLA_ERR_NULL;
+    if (!decode_shape_ok(B, H, num_splits) || S_max < 1 || Dv < 1 || !good_scale(scale)) return MLA_ERR_SHAPE;
+    if ((long long)B * S_max > (long long)INT_MAX / mla::kRow) return MLA_ERR_SHAPE;
+    if (Dv % 128 != 0 || Dv > 4096) return MLA_ERR_UNSUPPORTED;
+    if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(kv_cache) || !aligned16(seqlens) || !aligned16(w_uv) ||
+        !aligned16(o_v) || (lse && !aligned16(lse)) || (workspace && !aligned16(workspace)))
+        return MLA_ERR_ALIGN;
+    if (!workspace) return MLA_ERR_WORKSPACE;
+    const int cus = current_cu_count();
+    if (cus <= 0) return MLA_ERR_HIP;
+    const DecodeConfig c = decode_config(B, num_splits, cus, true);
+    const mla::PlanLayout L = mla::plan_layout(B, H, c.parts, c.slots);
+    if (workspace_bytes < L.total_bytes) return MLA_ERR_WORKSPACE;
+    return hip_status(mla::launch_mla_decode(
+        static_cast<const __bf16*>(q_lat), static_cast<const __bf16*>(q_rope), static_cast<const __bf16*>(kv_cache),
+        seqlens, static_cast<__bf16*>(o_v), lse, B, H, S_max, scale, num_splits, L, c.c0, c.t_min, workspace, stream,
+        static_cast<const __bf16*>(w_uv), Dv));
 }
 
 MLA_EXPORT mla_status_t mla_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B, int H,

@@ -28,6 +28,7 @@
 // split into blocks as well.  For Dn = 128 and 512 the q_nope rows of the
 // next 64-row block are loaded while the current block's MFMAs run.
 #include "common.h"
+#include "mla_merge.h"
 
 namespace mla {
 
@@ -184,6 +185,61 @@ __global__ __launch_bounds__(ABS_THREADS, KS == 16 ? 1 : 2) void mla_absorb_kern
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the split decode fused with the value up-projection.
+//
+// [MLA-FA3 article] fused dataflow figure: the value up-projection W_UV
+// belongs to the same in-place stage as W_UK, after the online-softmax
+// partial reduction.  Attention is linear in its values, so
+//   o_v[b, h, :] = o[b, h, :] W_UV[h],  o = the merged latent output.
+// The split kernel (value mode) leaves every piece of sequence b -- one for
+// an unsplit sequence -- as a bf16 partial in slot b + p (p = its part).
+// This kernel is the absorption kernel's per-head product with its B operand
+// built on the fly: each lane merges its row's partials in fp32 for the 8
+// latent dims it feeds (merge_row_init / merge_dims8, the same arithmetic as
+// the combine kernel), rounds them to bf16, and multiplies by the W_UV slab
+// held in LDS.  The merged latent row never goes to memory; the merged LSE
+// is written once per (b, h).
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(ABS_THREADS, 1) void mla_merge_up_kernel(
+    const int* __restrict__ ws, int seq_first, int seq_nsplit, const __bf16* __restrict__ o_part,
+    const float* __restrict__ lse_part, const __bf16* __restrict__ w_uv, __bf16* __restrict__ o_v,
+    float* __restrict__ lse, int B, int H, int Dv, int rows) {
+    constexpr int Dl = 32 * KS;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // [Dl][128] bf16, 256-byte rows, then staging
+    const int nb = (B + rows - 1) / rows;
+    int h, cb, rb;
+    abs_block(blockIdx.x, H, Dv / ABS_COLS, nb, h, cb, rb);
+    const int col0 = cb * ABS_COLS;
+    const int b_lo = rb * rows, b_hi = min(B, b_lo + rows);
+    const int w = wave_id();
+    const int lane = lane_id();
+    const int n = lane & 15, g = lane >> 4;
+    const int jj = n >> 2, qd = n & 3;
+
+    abs_load_w(w_uv, smem, h, col0, Dl, Dv, w, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int bb = b_lo; bb < b_hi; bb += 64) {
+        const int row = bb + 16 * w + n;
+        const int b = min(row, B - 1);
+        const int first = ws[seq_first + b], ns = ws[seq_nsplit + b];
+        auto rows_fn = [&](int s) -> size_t { return (size_t)(b + first + s) * H + h; };
+        const MergeRow mr = merge_row_init(lse_part, ns, rows_fn);
+        bf16x8 cur[KS];
+        merge_row_kk<KS>(o_part, lse_part, ns, rows_fn, g, mr, cur);
+        if (lse && cb == 0 && g == 0 && row < b_hi) lse[(size_t)b * H + h] = mr.lse;
+        f32x4 acc[ABS_COLS / 16];
+#pragma unroll
+        for (int db = 0; db < ABS_COLS / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) abs_kstep(smem, kk, g, jj, qd, cur[kk], acc);
+        abs_store_staged(o_v, acc, bb + 16 * w, b_hi, H, h, Dv, col0, smem + Dl * 256 + w * ABS_STG_BYTES, n, g,
+                         lane);
+    }
+}
+
 hipError_t ensure_smem_attr(const void* fn, int bytes);
 
 // Rows of q_nope per workgroup: all of them when the (head, column block)
@@ -211,6 +267,22 @@ static hipError_t launch_abs(const __bf16* q_nope, const __bf16* w_uk, __bf16* q
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(mla_absorb_kernel<KS>, dim3((unsigned)grid), dim3(ABS_THREADS), smem, stream, q_nope, w_uk,
                        q_lat, B, H, Dn, Dl, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_mla_merge_up(const int* ws, int seq_first, int seq_nsplit, const __bf16* o_part,
+                               const float* lse_part, const __bf16* w_uv, __bf16* o_v, float* lse, int B, int H,
+                               int Dv, hipStream_t stream) {
+    constexpr int KS = 16;  // Dl = 512
+    const int smem = 32 * KS * ABS_COLS * 2 + 4 * ABS_STG_BYTES;
+    hipError_t e = ensure_smem_attr((const void*)mla_merge_up_kernel<KS>, smem);
+    if (e != hipSuccess) return e;
+    const int nc = Dv / ABS_COLS;
+    const int rows = abs_rows(B, H, nc);
+    const long long grid = (long long)nc * H * ((B + rows - 1) / rows);
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(mla_merge_up_kernel<KS>, dim3((unsigned)grid), dim3(ABS_THREADS), smem, stream, ws, seq_first,
+                       seq_nsplit, o_part, lse_part, w_uv, o_v, lse, B, H, Dv, rows);
     return hipGetLastError();
 }
 

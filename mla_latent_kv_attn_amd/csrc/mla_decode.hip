@@ -43,6 +43,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "mla_merge.h"
 #include "mla_plan.h"
 
 namespace mla {
@@ -88,14 +89,21 @@ struct PlanArgs {
 //      t = max(ceil(C / parts), ceil(max_n / (num_splits - 1)), t_min, 1),
 //    which bounds every sequence to at most num_splits parts.  With
 //    num_splits == 1 each sequence gets its own part (t = max_n + c0).
-//    One workgroup of 256 threads; each thread handles four consecutive
-//    sequences of a 1024-sequence chunk, so the offsets need one scan per
-//    chunk (within each wave by lane shuffles, then over the four wave
-//    totals).  The first sequence of each part is found with LDS atomics.
+//    A block of 256 threads scans the lengths: each thread handles four
+//    consecutive sequences of a 1024-sequence chunk, so the offsets need one
+//    scan per chunk (within each wave by lane shuffles, then over the four
+//    wave totals).  The first sequence of each part is found with LDS
+//    atomics.
+//    Where it runs: with num_splits >= 2 and B <= 1024 every split workgroup
+//    computes the plan itself, in LDS, before its first tile (workgroup 0
+//    also writes it to the workspace for the combine); otherwise a one-block
+//    plan kernel writes it to the workspace first.  The separate launch cost
+//    5.5-6.2 us per call on MI355X, the in-kernel scan about 1 us.
 // ---------------------------------------------------------------------------
 constexpr int PLAN_THREADS = 256;
 constexpr int PLAN_PER = 4;
 constexpr int PLAN_CHUNK = PLAN_THREADS * PLAN_PER;
+static_assert(PLAN_THREADS == 256, "the split kernel's block runs the in-kernel plan");
 
 __device__ __forceinline__ int wave_incl_sum(int x, int lane) {
 #pragma unroll
@@ -116,60 +124,106 @@ __device__ __forceinline__ int wave_sum(int x) {
     return x;
 }
 
+// One chunk of the cost-line scan: thread tid handles sequences
+// base + 4 tid + k (k < 4).  Returns their clamped lengths, tiles and
+// cost-line starts (carry = cost of every sequence before the chunk), and
+// the chunk's total cost, largest n and clamp count (block-uniform).
+// s_red: 12 ints of LDS.
+struct ChunkScan {
+    int total, max_n, clamped;
+};
+__device__ ChunkScan plan_scan_chunk(const int* __restrict__ seqlens, int base, int B, int S_max, int c0, int carry,
+                                     int (&n)[PLAN_PER], int (&len)[PLAN_PER], int (&start)[PLAN_PER], int* s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int NW = PLAN_THREADS / 64;
+    int cost[PLAN_PER], sum = 0, mx = 0, ncl = 0;
+#pragma unroll
+    for (int k = 0; k < PLAN_PER; ++k) {
+        const int b = base + PLAN_PER * tid + k;
+        n[k] = 0;
+        len[k] = 0;
+        if (b < B) {
+            const int raw = seqlens[b];
+            len[k] = min(max(raw, 0), S_max);
+            ncl += len[k] != raw;
+            n[k] = (len[k] + kDecodeTile - 1) / kDecodeTile;
+            mx = max(mx, n[k]);
+        }
+        cost[k] = n[k] > 0 ? n[k] + c0 : 0;
+        sum += cost[k];
+    }
+    const int incl = wave_incl_sum(sum, lane);
+    mx = wave_max(mx);
+    ncl = wave_sum(ncl);
+    if (lane == 63) s_red[wv] = incl;
+    if (lane == 0) {
+        s_red[NW + wv] = mx;
+        s_red[2 * NW + wv] = ncl;
+    }
+    __syncthreads();
+    int woff = 0;
+    ChunkScan r{0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        woff += i < wv ? s_red[i] : 0;
+        r.total += s_red[i];
+        r.max_n = max(r.max_n, s_red[NW + i]);
+        r.clamped += s_red[2 * NW + i];
+    }
+    __syncthreads();  // s_red is rewritten by the next chunk
+    int acc = carry + woff + incl - sum;  // cost of all sequences before this thread's first
+#pragma unroll
+    for (int k = 0; k < PLAN_PER; ++k) {
+        start[k] = acc + c0;
+        acc += cost[k];
+    }
+    return r;
+}
+
+__device__ __forceinline__ int plan_line_t(int C, int parts, int max_n, int num_splits, int t_min) {
+    return max(max((C + parts - 1) / parts, (max_n + num_splits - 2) / (num_splits - 1)), max(t_min, 1));
+}
+
+__device__ __forceinline__ void plan_write_header(int* ws, int parts_used, int t, int C, int c0, bool whole,
+                                                  int nparts, int clamped, int max_n, int B, int t_min,
+                                                  int num_splits) {
+    ws[kHdrPartsUsed] = parts_used;
+    ws[kHdrT] = t;
+    ws[kHdrC] = C;
+    ws[kHdrTile] = kDecodeTile;
+    ws[kHdrC0] = c0;
+    ws[kHdrMode] = whole ? 1 : 0;
+    ws[kHdrParts] = nparts;
+    ws[kHdrClamped] = clamped;
+    ws[kHdrMaxN] = max_n;
+    ws[kHdrB] = B;
+    ws[kHdrTMin] = t_min;
+    ws[kHdrNumSplits] = num_splits;
+}
+
 __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(const int* __restrict__ seqlens, int* __restrict__ ws,
                                                                int B, int S_max, int parts, int c0, int t_min,
                                                                int num_splits, PlanArgs a) {
-    __shared__ int s_wsum[PLAN_THREADS / 64], s_wmax[PLAN_THREADS / 64], s_wclamp[PLAN_THREADS / 64];
+    __shared__ int s_red[12];
     __shared__ int s_pfs[kPlanMaxParts];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int my_n[PLAN_PER], my_start[PLAN_PER];  // kept for the second pass when B <= PLAN_CHUNK
-    int carry = 0, mx = 0, nclamp = 0;
+    const int tid = threadIdx.x;
+    int my_n[PLAN_PER], my_len[PLAN_PER], my_start[PLAN_PER];  // kept for the second pass when B <= PLAN_CHUNK
+    int carry = 0, max_n = 0, clamped = 0;
     for (int base = 0; base < B; base += PLAN_CHUNK) {
-        int cost[PLAN_PER], sum = 0;
+        const ChunkScan cs = plan_scan_chunk(seqlens, base, B, S_max, c0, carry, my_n, my_len, my_start, s_red);
 #pragma unroll
         for (int k = 0; k < PLAN_PER; ++k) {
             const int b = base + PLAN_PER * tid + k;
-            int n = 0;
             if (b < B) {
-                const int raw = seqlens[b];
-                const int len = min(max(raw, 0), S_max);
-                nclamp += len != raw;
-                n = (len + kDecodeTile - 1) / kDecodeTile;
-                ws[a.seq_len + b] = len;
-                ws[a.seq_n + b] = n;
-                mx = max(mx, n);
+                ws[a.seq_len + b] = my_len[k];
+                ws[a.seq_n + b] = my_n[k];
+                ws[a.seq_start + b] = my_start[k];
             }
-            my_n[k] = n;
-            cost[k] = n > 0 ? n + c0 : 0;
-            sum += cost[k];
         }
-        const int incl = wave_incl_sum(sum, lane);
-        if (lane == 63) s_wsum[wv] = incl;
-        __syncthreads();
-        int woff = 0, total = 0;
-#pragma unroll
-        for (int i = 0; i < PLAN_THREADS / 64; ++i) {
-            woff += i < wv ? s_wsum[i] : 0;
-            total += s_wsum[i];
-        }
-        __syncthreads();  // s_wsum is rewritten by the next chunk
-        int acc = carry + woff + incl - sum;  // cost of all sequences before this thread's first
-#pragma unroll
-        for (int k = 0; k < PLAN_PER; ++k) {
-            const int b = base + PLAN_PER * tid + k;
-            my_start[k] = acc + c0;
-            if (b < B) ws[a.seq_start + b] = my_start[k];
-            acc += cost[k];
-        }
-        carry += total;
+        carry += cs.total;
+        max_n = max(max_n, cs.max_n);
+        clamped += cs.clamped;
     }
-    mx = wave_max(mx);
-    nclamp = wave_sum(nclamp);
-    if (lane == 0) { s_wmax[wv] = mx; s_wclamp[wv] = nclamp; }
-    __syncthreads();
-    int max_n = 0, clamped = 0;
-#pragma unroll
-    for (int i = 0; i < PLAN_THREADS / 64; ++i) { max_n = max(max_n, s_wmax[i]); clamped += s_wclamp[i]; }
     const bool whole = num_splits == 1;
     int t, C, parts_used, nparts;
     if (whole) {
@@ -179,7 +233,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(const int* __res
         nparts = B;
     } else {
         C = carry;
-        t = max(max((C + parts - 1) / parts, (max_n + num_splits - 2) / (num_splits - 1)), max(t_min, 1));
+        t = plan_line_t(C, parts, max_n, num_splits, t_min);
         parts_used = (C + t - 1) / t;
         nparts = parts;  // <= kPlanMaxParts (checked by the host)
         for (int p = tid; p < nparts; p += PLAN_THREADS) s_pfs[p] = B;
@@ -212,20 +266,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void mla_plan_kernel(const int* __res
         __syncthreads();
         for (int p = tid; p < nparts; p += PLAN_THREADS) ws[a.part_first_seq + p] = s_pfs[p];
     }
-    if (tid == 0) {
-        ws[kHdrPartsUsed] = parts_used;
-        ws[kHdrT] = t;
-        ws[kHdrC] = C;
-        ws[kHdrTile] = kDecodeTile;
-        ws[kHdrC0] = c0;
-        ws[kHdrMode] = whole ? 1 : 0;
-        ws[kHdrParts] = nparts;
-        ws[kHdrClamped] = clamped;
-        ws[kHdrMaxN] = max_n;
-        ws[kHdrB] = B;
-        ws[kHdrTMin] = t_min;
-        ws[kHdrNumSplits] = num_splits;
-    }
+    if (tid == 0) plan_write_header(ws, parts_used, t, C, c0, whole, nparts, clamped, max_n, B, t_min, num_splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -241,7 +282,8 @@ struct DecodeCtx {
     const __bf16* q_lat;
     const __bf16* q_rope;
     const __bf16* cache;
-    const int* ws;
+    int* ws;
+    const int* seqlens;
     __bf16* o_part;
     float* lse_part;
     __bf16* o;
@@ -249,6 +291,11 @@ struct DecodeCtx {
     int H, S_max;
     float c_log2;
     PlanArgs a;
+    // In-kernel plan (fused = 1): the plan kernel's arguments.
+    int fused, B, parts, c0, t_min, num_splits;
+    // Value up-projection mode (vmode = 1): every piece, split or not, writes
+    // its partial to slot b + p; the merge happens in the up-projection.
+    int vmode;
 };
 
 // Copy one 32-token tile to LDS: copy i (0..36) of 64 chunks is issued by
@@ -729,10 +776,10 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
         const int head = hblk + 16 * (2 * w + h) + n;
         if (act && g == 0) {
             const float lse_v = (st.m[h] + __builtin_log2f(lsum)) * kLn2;
-            if (nsplit == 1) {
+            if (nsplit == 1 && !x.vmode) {
                 if (x.lse) x.lse[(size_t)b * H + head] = lse_v;
             } else {
-                const int slot = 2 * p + (first_in_part ? 0 : 1);
+                const int slot = x.vmode ? b + p : 2 * p + (first_in_part ? 0 : 1);
                 x.lse_part[(size_t)slot * H + head] = lse_v;
             }
         }
@@ -750,10 +797,10 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     wait_lgkm<0>();
     // Row r of the wave's staging area is head hblk + 32w + r.
     __bf16* obase;
-    if (nsplit == 1) {
+    if (nsplit == 1 && !x.vmode) {
         obase = x.o + ((size_t)b * H + hblk + 32 * w) * kLatent;
     } else {
-        const int slot = 2 * p + (first_in_part ? 0 : 1);
+        const int slot = x.vmode ? b + p : 2 * p + (first_in_part ? 0 : 1);
         obase = x.o_part + ((size_t)slot * H + hblk + 32 * w) * kLatent;
     }
     const uint32_t ra = stg + (uint32_t)(16 * lane);
@@ -776,33 +823,134 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
     lds_barrier();
 }
 
+// Workgroups are dealt to the eight XCDs round-robin by id, and each XCD has
+// its own L2.  Part p of the plan runs on the workgroup whose id places
+// consecutive parts on one XCD: XCD x takes the parts
+// [x q + min(x, r), ...) with q = n / 8, r = n % 8, so the parts that share a
+// sequence (and its query block) mostly share an L2.  Only the speed depends
+// on the dealing order; any bijection gives the same results.
+__host__ __device__ constexpr int xcd_part(int id, int n) {
+    const int x = id & 7, k = id >> 3, q = n >> 3, r = n & 7;
+    return x * q + (x < r ? x : r) + k;
+}
+constexpr bool xcd_part_is_bijection(int n) {
+    bool seen[kPlanMaxParts] = {};
+    for (int id = 0; id < n; ++id) {
+        const int p = xcd_part(id, n);
+        if (p < 0 || p >= n || seen[p]) return false;
+        seen[p] = true;
+    }
+    return true;
+}
+static_assert(xcd_part_is_bijection(1) && xcd_part_is_bijection(7) && xcd_part_is_bijection(8) &&
+                  xcd_part_is_bijection(10) && xcd_part_is_bijection(255) && xcd_part_is_bijection(256) &&
+                  xcd_part_is_bijection(1000) && xcd_part_is_bijection(kPlanMaxParts),
+              "part mapping");
+
+// LDS after the tile ring: the in-kernel plan's per-sequence n, start and
+// len (PLAN_CHUNK each); read by the piece loop for the whole kernel.
+constexpr int DEC_PLAN_LDS = 3 * PLAN_CHUNK * 4;
+constexpr int DEC_SMEM_TOTAL = DEC_SMEM + DEC_PLAN_LDS;
+static_assert(DEC_SMEM_TOTAL <= 160 * 1024, "LDS");
+static_assert(PLAN_THREADS == DEC_THREADS, "the split workgroup runs the plan scan");
+
+// In-kernel plan (line mode, B <= PLAN_CHUNK): every workgroup scans the
+// lengths into LDS.  Returns (block-uniform) t, parts_used and the first
+// sequence of part p; workgroup (0, 0) also writes the whole plan to the
+// workspace, as the plan kernel would, for the combine kernel.  Uses the
+// start of the ring as scratch; a barrier ends it before any tile copy.
+__device__ void dec_plan_in_kernel(const DecodeCtx& x, char* smem, int p, int& t, int& parts_used, int& b0) {
+    int* l_n = reinterpret_cast<int*>(smem + DEC_SMEM);
+    int* l_start = l_n + PLAN_CHUNK;
+    int* l_len = l_start + PLAN_CHUNK;
+    int* s_red = reinterpret_cast<int*>(smem);    // 12 ints
+    int* s_b0 = s_red + 12;                       // 1 int
+    int* s_pfs = s_red + 16;                      // parts ints (workgroup 0)
+    const int tid = threadIdx.x, B = x.B, c0 = x.c0;
+    int n[PLAN_PER], len[PLAN_PER], start[PLAN_PER];
+    const ChunkScan cs = plan_scan_chunk(x.seqlens, 0, B, x.S_max, c0, 0, n, len, start, s_red);
+    const int C = cs.total;
+    t = plan_line_t(C, x.parts, cs.max_n, x.num_splits, x.t_min);
+    parts_used = (C + t - 1) / t;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    if (tid == 0) *s_b0 = B;
+    if (writer)
+        for (int q = tid; q < x.parts; q += PLAN_THREADS) s_pfs[q] = B;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PLAN_PER; ++k) {
+        const int b = PLAN_PER * tid + k;
+        if (b >= B) continue;
+        l_n[b] = n[k];
+        l_start[b] = start[k];
+        l_len[b] = len[k];
+        const int first = n[k] > 0 ? start[k] / t : 0;
+        const int ns = n[k] > 0 ? (start[k] + n[k] - 1) / t - first + 1 : 0;
+        if (ns > 0 && first <= p && p < first + ns) atomicMin(s_b0, b);
+        if (writer) {
+            int* ws = x.ws;
+            ws[x.a.seq_len + b] = len[k];
+            ws[x.a.seq_n + b] = n[k];
+            ws[x.a.seq_start + b] = start[k];
+            ws[x.a.seq_first + b] = first;
+            ws[x.a.seq_nsplit + b] = ns;
+            for (int q = first; q < first + ns; ++q) atomicMin(&s_pfs[q], b);
+        }
+    }
+    __syncthreads();
+    b0 = *s_b0;
+    if (writer) {
+        for (int q = tid; q < x.parts; q += PLAN_THREADS) x.ws[x.a.part_first_seq + q] = s_pfs[q];
+        if (tid == 0)
+            plan_write_header(x.ws, parts_used, t, C, c0, false, x.parts, cs.clamped, cs.max_n, B, x.t_min,
+                              x.num_splits);
+    }
+    __syncthreads();  // the ring's scratch is free again
+}
+
 // Pieces of part p, found without a chain of dependent loads: lane i reads
 // the plan entries of sequence b0 + i (b0 = the part's first sequence) in one
 // round trip, and a ballot lists the lanes whose sequence has tiles in the
 // part.  Only the ballot mask stays live across pieces; each piece re-reads
-// its sequence's entries with scalar loads.  A part spans more than 64
-// sequences only when they are very short; then the next 64 are read the
-// same way.
+// its sequence's entries.  A part spans more than 64 sequences only when
+// they are very short; then the next 64 are read the same way.  The plan
+// entries come from LDS (in-kernel plan) or from the workspace.
 __global__ __launch_bounds__(DEC_THREADS, 1) void mla_split_kernel(DecodeCtx x) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int p = blockIdx.x;
-    const int* ws = x.ws;
-    const int parts_used = ws[kHdrPartsUsed];
+    const int p = xcd_part(blockIdx.x, gridDim.x);
+    const int* pl_n;
+    const int* pl_start;
+    const int* pl_len;
+    int t, parts_used, b0, B, whole;
+    if (x.fused) {
+        dec_plan_in_kernel(x, smem, p, t, parts_used, b0);
+        B = x.B;
+        whole = 0;
+        pl_n = reinterpret_cast<const int*>(smem + DEC_SMEM);
+        pl_start = pl_n + PLAN_CHUNK;
+        pl_len = pl_start + PLAN_CHUNK;
+    } else {
+        const int* ws = x.ws;
+        parts_used = ws[kHdrPartsUsed];
+        t = ws[kHdrT];
+        whole = ws[kHdrMode];
+        B = ws[kHdrB];
+        b0 = p < parts_used ? ws[x.a.part_first_seq + p] : B;
+        pl_n = ws + x.a.seq_n;
+        pl_start = ws + x.a.seq_start;
+        pl_len = ws + x.a.seq_len;
+    }
     if (p >= parts_used) return;
-    const int t = ws[kHdrT];
-    const int whole = ws[kHdrMode];
-    const int B = ws[kHdrB];
     const int pos_lo = p * t, pos_hi = pos_lo + t;
     const int lane = lane_id();
-    const int b0 = ws[x.a.part_first_seq + p];
     for (int base = b0; base < B; base += 64) {
         uint64_t pieces, more;
         {
             const int b = base + lane;
             int nb = 0, sb = pos_hi;
             if (b < B && (!whole || b == b0)) {
-                nb = ws[x.a.seq_n + b];
-                sb = ws[x.a.seq_start + b];
+                nb = pl_n[b];
+                sb = pl_start[b];
             }
             pieces = __builtin_amdgcn_ballot_w64(nb > 0 && max(sb, pos_lo) < min(sb + nb, pos_hi));
             more = __builtin_amdgcn_ballot_w64(nb > 0 && sb >= pos_hi);
@@ -810,9 +958,12 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void mla_split_kernel(DecodeCtx x) 
         while (pieces) {
             const int i = __builtin_ctzll(pieces);
             pieces &= pieces - 1;
-            const int b = base + i;  // uniform: plan entries come through the scalar cache
-            const int nb = ws[x.a.seq_n + b], sb = ws[x.a.seq_start + b];
-            const int ln = ws[x.a.seq_len + b], ns = ws[x.a.seq_nsplit + b];
+            const int b = __builtin_amdgcn_readfirstlane(base + i);
+            const int nb = __builtin_amdgcn_readfirstlane(pl_n[b]);
+            const int sb = __builtin_amdgcn_readfirstlane(pl_start[b]);
+            const int ln = __builtin_amdgcn_readfirstlane(pl_len[b]);
+            const int first = sb / t;
+            const int ns = whole ? 1 : (sb + nb - 1) / t - first + 1;
             const int lo = max(sb, pos_lo) - sb, hi = min(sb + nb, pos_hi) - sb;
             dec_piece(x, smem, p, b, lo, hi, ln, ns, b == b0);
         }
@@ -830,65 +981,13 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void mla_split_kernel(DecodeCtx x) 
 constexpr int CMB_THREADS = 256;
 constexpr int CMB_HEADS = CMB_THREADS / (kLatent / 8);  // 4
 
-__device__ __forceinline__ void load8(const __bf16* p, float* v) {
-    const bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)t[i];
-}
-__device__ __forceinline__ void load8(const float* p, float* v) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-}
-
 // rows(s) gives the row index of split s in lse_part (and, times 512, in o_part).
 template <typename PT, typename RowFn>
 __device__ __forceinline__ void combine_head(const PT* o_part, const float* lse_part, int nsplit, RowFn rows,
                                              __bf16* o_row, float* lse_out, int d8) {
-    // One pass, four splits at a time: the loads of a chunk are independent
-    // and issued together; the running max M rescales what is summed so far.
-    float M = -INFINITY, W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-        float ls[4], v[4][8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            ls[k] = -INFINITY;
-            if (s0 + k < nsplit) {
-                const size_t r = rows(s0 + k);
-                ls[k] = lse_part[r];
-                load8(o_part + r * kLatent + 8 * d8, v[k]);
-            }
-        }
-        const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
-        if (m_new == -INFINITY) continue;  // every split so far is empty
-        const float sc = (M == -INFINITY) ? 0.f : __expf(M - m_new);
-        W *= sc;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= sc;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (ls[k] == -INFINITY) continue;  // empty split or past the end: weight 0
-            const float wgt = __expf(ls[k] - m_new);
-            W += wgt;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wgt, v[k][i], acc[i]);
-        }
-        M = m_new;
-    }
-    bf16x8 out;
-    if (M == -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = to_bf16(0.f);
-        *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = out;
-        if (lse_out && d8 == 0) *lse_out = -INFINITY;
-        return;
-    }
-    const float inv = 1.f / W;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = to_bf16(acc[i] * inv);
-    *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = out;
-    if (lse_out && d8 == 0) *lse_out = M + __logf(W);
+    const MergeRow mr = merge_row_init(lse_part, nsplit, rows);
+    *reinterpret_cast<bf16x8*>(o_row + 8 * d8) = merge_dims8(o_part, lse_part, nsplit, rows, d8, mr);
+    if (lse_out && d8 == 0) *lse_out = mr.lse;
 }
 
 // Partials of the split kernel: slot-major [slots][H][512] bf16, lse [slots][H].
@@ -990,16 +1089,34 @@ static PlanArgs plan_args(const PlanLayout& L) {
     return a;
 }
 
+hipError_t launch_mla_merge_up(const int* ws, int seq_first, int seq_nsplit, const __bf16* o_part,
+                               const float* lse_part, const __bf16* w_uv, __bf16* o_v, float* lse, int B, int H,
+                               int Dv, hipStream_t stream);
+
+// w_uv == nullptr: the latent decode (plan, split kernel, combine) writing
+// o [B, H, 512].  w_uv != nullptr: the same split kernel in value mode, then
+// the merge fused with the value up-projection, writing o_v [B, H, Dv].
 hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __bf16* cache, const int* seqlens,
                              __bf16* o, float* lse, int B, int H, int S_max, float scale, int num_splits,
-                             const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream) {
-    hipError_t e = ensure_smem_attr((const void*)mla_split_kernel, DEC_SMEM);
+                             const PlanLayout& L, int c0, int t_min, void* workspace, hipStream_t stream,
+                             const __bf16* w_uv, int Dv) {
+    hipError_t e = ensure_smem_attr((const void*)mla_split_kernel, DEC_SMEM_TOTAL);
     if (e != hipSuccess) return e;
     int* ws = static_cast<int*>(workspace);
     const PlanArgs a = plan_args(L);
-    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, seqlens, ws, B, S_max, L.parts, c0, t_min,
-                       num_splits, a);
+    const bool fused = num_splits >= 2 && B <= PLAN_CHUNK;
+    if (!fused)
+        hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, seqlens, ws, B, S_max, L.parts,
+                           c0, t_min, num_splits, a);
     DecodeCtx x;
+    x.seqlens = seqlens;
+    x.fused = fused ? 1 : 0;
+    x.B = B;
+    x.parts = L.parts;
+    x.c0 = c0;
+    x.t_min = t_min;
+    x.num_splits = num_splits;
+    x.vmode = w_uv ? 1 : 0;
     x.q_lat = q_lat;
     x.q_rope = q_rope;
     x.cache = cache;
@@ -1013,7 +1130,13 @@ hipError_t launch_mla_decode(const __bf16* q_lat, const __bf16* q_rope, const __
     x.c_log2 = scale * kLog2e;
     x.a = a;
     const int hblocks = (H + kDecodeHeadsPerWG - 1) / kDecodeHeadsPerWG;
-    hipLaunchKernelGGL(mla_split_kernel, dim3(L.parts, hblocks), dim3(DEC_THREADS), DEC_SMEM, stream, x);
+    hipLaunchKernelGGL(mla_split_kernel, dim3(L.parts, hblocks), dim3(DEC_THREADS), DEC_SMEM_TOTAL, stream, x);
+    if (w_uv) {
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_mla_merge_up(ws, a.seq_first, a.seq_nsplit, x.o_part, x.lse_part, w_uv, o, lse, B, H, Dv,
+                                   stream);
+    }
     hipLaunchKernelGGL(mla_combine_slots_kernel, dim3(B, (H + CMB_HEADS - 1) / CMB_HEADS), dim3(CMB_THREADS), 0,
                        stream, ws, x.o_part, x.lse_part, o, lse, H, a);
     return hipGetLastError();

@@ -11,7 +11,7 @@
 
 namespace mla {
 
-constexpr int kDecodeTile = 64;        // cache tokens per tile
+constexpr int kDecodeTile = 32;        // cache tokens per plan tile (one LDS tile of the split kernel)
 constexpr int kDecodeHeadsPerWG = 128;  // heads one split workgroup serves
 constexpr int kLatent = 512;
 constexpr int kRope = 64;

@@ -355,3 +355,90 @@ def test_split_partials_cost_at_most_one_bf16_rounding():
     check_bf16(o32, Or, "O split")
     check_lse(l32, Lr, "LSE split")
     check_lse(l1, Lr, "LSE unsplit")
+
+
+# ------------------------------------------- decode + value up-projection ----
+def decode_v(d, w_uv, num_splits):
+    ql, qr, c, sl = (d[k].to(DEV) for k in ("q_lat", "q_rope", "cache", "seqlens"))
+    B, H, _ = ql.shape
+    ws = binding.alloc_decode_v_workspace(B, H, num_splits, DEV)
+    o_v, l = binding.mla_decode_fwd_v(ql, qr, c, sl, w_uv.to(DEV), SCALE, num_splits, workspace=ws)
+    sync()
+    return o_v, l, ws
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 32])
+def test_decode_v_small(case, num_splits):
+    # The fused merge + W_UV path against the oracle's attention over
+    # explicitly decompressed values, and bitwise against the unfused path
+    # (mla_decode_fwd, then mla_up_proj_v).
+    B, H, lens, S = CASES[case]
+    say(f"decode_v B={B} H={H} lens={lens} S_max={S} num_splits={num_splits}")
+    d = workloads.decode_inputs(B, H, lens, S_max=S, seed=2700 + case)
+    w_uv = workloads.w_uv_weights(H=H, seed=2710 + case)
+    o_v, l, ws = decode_v(d, w_uv, num_splits)
+    check_plan(ws, d, num_splits)
+    ref = OM.mla_decode_values_explicit_ref(np64(d["q_lat"]), np64(d["q_rope"]), np64(w_uv), np64(d["cache"]),
+                                            lens, SCALE)
+    check_bf16(o_v, ref, "o_v")
+    _, Lr = oracle_decode(d)
+    check_lse(l, Lr, "LSE")
+    o_lat, l2, _ = decode(d, num_splits)
+    o_v2 = binding.mla_up_proj_v(o_lat, w_uv.to(DEV))
+    sync()
+    assert torch.equal(o_v, o_v2), "fused and unfused value paths differ"
+    assert torch.equal(l, l2)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o_v[b] == 0) and torch.all(torch.isneginf(l[b]))
+
+
+@pytest.mark.parametrize("num_splits", [1, 8])
+def test_decode_v_many_short_sequences(num_splits):
+    # B beyond the in-kernel plan (plan kernel path) and many empty sequences.
+    B, H, S = 1500, 16, 80
+    lens = workloads.random_seqlens(B, 0, S, 2720).tolist()
+    d = workloads.decode_inputs(B, H, lens, S_max=S, seed=2721)
+    w_uv = workloads.w_uv_weights(H=H, Dv=256, seed=2722)
+    o_v, l, ws = decode_v(d, w_uv, num_splits)
+    check_plan(ws, d, num_splits)
+    o_lat, l2, _ = decode(d, num_splits)
+    o_v2 = binding.mla_up_proj_v(o_lat, w_uv.to(DEV))
+    sync()
+    assert torch.equal(o_v, o_v2) and torch.equal(l, l2)
+    idx = [0, 1, 2, 700, B - 1] + [b for b, L in enumerate(lens) if L == 0][:3]
+    ref = OM.mla_decode_values_explicit_ref(np64(d["q_lat"][idx]), np64(d["q_rope"][idx]), np64(w_uv),
+                                            np64(d["cache"][idx]), [lens[i] for i in idx], SCALE)
+    check_bf16(o_v[idx], ref, "o_v(sampled)")
+
+
+def test_decode_v_varlen_workload_end_to_end(varlen):
+    # The full variable-length step with the value output: GPU absorption ->
+    # fused decode + W_UV, against the oracle (own absorption, own bf16 q_lat,
+    # decode, projection), all 256 sequences; and bitwise against the
+    # unfused path.
+    d = varlen
+    say("absorb + decode_v mla_varlen (B=256 H=128 Dv=128), all sequences")
+    w_uv = workloads.w_uv_weights(H=128)
+    ql = binding.mla_absorb_q(d["q_nope"].to(DEV), d["w_uk"].to(DEV))
+    qr, c, sl = d["q_rope"].to(DEV), d["cache"].to(DEV), d["seqlens"].to(DEV)
+    ws = binding.alloc_decode_v_workspace(256, 128, 32, DEV)
+    o_v, l = binding.mla_decode_fwd_v(ql, qr, c, sl, w_uv.to(DEV), SCALE, 32, workspace=ws)
+    o_lat, l2 = binding.mla_decode_fwd(ql, qr, c, sl, SCALE, 32)
+    o_v2 = binding.mla_up_proj_v(o_lat, w_uv.to(DEV))
+    sync()
+    assert torch.equal(o_v, o_v2) and torch.equal(l, l2), "fused and unfused value paths differ"
+    del c
+    lens = d["seqlens"].tolist()
+    w_uk, w_uv64 = np64(d["w_uk"]), np64(w_uv)
+    ref = np.empty((256, 128, 128))
+    Lr = np.empty((256, 128))
+    for b0 in range(0, 256, 16):
+        idx = list(range(b0, b0 + 16))
+        Lm = max(lens[i] for i in idx)
+        Ob, Lr[idx] = OM.absorb_decode_ref(np64(d["q_nope"][idx]), w_uk, np64(d["q_rope"][idx]),
+                                           np64(d["cache"][idx, :Lm]), [lens[i] for i in idx], SCALE)
+        ref[idx] = OM.up_project_v_ref(Ob, w_uv64)
+    check_bf16(o_v, ref, "o_v (256 sequences)")
+    check_lse(l, Lr, "LSE (256 sequences)")
