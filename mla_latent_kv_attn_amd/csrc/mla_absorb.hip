@@ -218,17 +218,30 @@ __global__ __launch_bounds__(ABS_THREADS, 1) void mla_merge_up_kernel(
     const int n = lane & 15, g = lane >> 4;
     const int jj = n >> 2, qd = n & 3;
 
+    // The slab's copies are issued first and land while the first row block
+    // is merged; the next block's plan entries are read one block ahead.
     abs_load_w(w_uv, smem, h, col0, Dl, Dv, w, lane);
-    wait_vmcnt<0>();
-    __syncthreads();
+    auto entries = [&](int bb, int& b, int& first, int& ns) {
+        b = min(bb + 16 * w + n, B - 1);
+        first = ws[seq_first + b];
+        ns = ws[seq_nsplit + b];
+    };
+    int nb_b, nb_first, nb_ns;
+    entries(b_lo, nb_b, nb_first, nb_ns);
+    bool slab_ready = false;
     for (int bb = b_lo; bb < b_hi; bb += 64) {
         const int row = bb + 16 * w + n;
-        const int b = min(row, B - 1);
-        const int first = ws[seq_first + b], ns = ws[seq_nsplit + b];
+        const int b = nb_b, first = nb_first, ns = nb_ns;
+        if (bb + 64 < b_hi) entries(bb + 64, nb_b, nb_first, nb_ns);
         auto rows_fn = [&](int s) -> size_t { return (size_t)(b + first + s) * H + h; };
         const MergeRow mr = merge_row_init(lse_part, ns, rows_fn);
         bf16x8 cur[KS];
         merge_row_kk<KS>(o_part, lse_part, ns, rows_fn, g, mr, cur);
+        if (!slab_ready) {  // the merge's loads were waited for, and with them the earlier slab copies
+            wait_vmcnt<0>();
+            __syncthreads();
+            slab_ready = true;
+        }
         if (lse && cb == 0 && g == 0 && row < b_hi) lse[(size_t)b * H + h] = mr.lse;
         f32x4 acc[ABS_COLS / 16];
 #pragma unroll

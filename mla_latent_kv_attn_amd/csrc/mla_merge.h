@@ -45,8 +45,10 @@ __device__ __forceinline__ MergeRow merge_row_init(const float* lse_part, int ns
 #pragma unroll
         for (int k = 0; k < 4; ++k) ls[k] = s0 + k < nsplit ? lse_part[rows(s0 + k)] : -INFINITY;
     };
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float first4[4];
+    lse4(0, first4);
+    float M = fmaxf(-INFINITY, fmaxf(fmaxf(first4[0], first4[1]), fmaxf(first4[2], first4[3])));
+    for (int s0 = 4; s0 < nsplit; s0 += 4) {
         float ls[4];
         lse4(s0, ls);
         M = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
@@ -60,7 +62,10 @@ __device__ __forceinline__ MergeRow merge_row_init(const float* lse_part, int ns
         return r;
     }
     float W = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // the first four are still in registers
+        if (first4[k] != -INFINITY) W += __expf(first4[k] - M);
+    for (int s0 = 4; s0 < nsplit; s0 += 4) {
         float ls[4];
         lse4(s0, ls);
 #pragma unroll

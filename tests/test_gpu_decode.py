@@ -442,3 +442,66 @@ def test_decode_v_varlen_workload_end_to_end(varlen):
         ref[idx] = OM.up_project_v_ref(Ob, w_uv64)
     check_bf16(o_v, ref, "o_v (256 sequences)")
     check_lse(l, Lr, "LSE (256 sequences)")
+
+
+# ----------------------------------- workspace reuse between calls ----
+def _fill(dst, src):
+    dst.copy_(src.to(DEV))
+
+
+def test_decode_graph_replays_with_new_inputs():
+    # A captured decode replayed with new inputs copied into the captured
+    # buffers must equal an eager call on those inputs: nothing of an earlier
+    # replay (plan, partials) may leak into the next.
+    B, H, ns, S = 5, 128, 7, 2100
+    lens = [900, 1, 0, 2100, 333]
+    sets = [workloads.decode_inputs(B, H, lens, S_max=S, seed=2800 + i) for i in range(4)]
+    ql = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    qr = torch.empty((B, H, 64), dtype=torch.bfloat16, device=DEV)
+    c = torch.empty((B, S, 576), dtype=torch.bfloat16, device=DEV)
+    sl = torch.empty((B,), dtype=torch.int32, device=DEV)
+    ws = binding.alloc_decode_workspace(B, H, ns, DEV)
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    for t, k in ((ql, "q_lat"), (qr, "q_rope"), (c, "cache"), (sl, "seqlens")):
+        _fill(t, sets[0][k])
+    binding.mla_decode_fwd(ql, qr, c, sl, SCALE, ns, workspace=ws, o=o, lse=lse)
+    sync()
+    plan = binding.read_plan(ws, B)
+    assert any(n == 1 for n in plan["nsplit"]) and max(plan["nsplit"]) > 2, plan["nsplit"]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.mla_decode_fwd(ql, qr, c, sl, SCALE, ns, workspace=ws, o=o, lse=lse)
+    for rep in range(6):
+        d = sets[rep % 4]
+        for t, k in ((ql, "q_lat"), (qr, "q_rope"), (c, "cache"), (sl, "seqlens")):
+            _fill(t, d[k])
+        sync()
+        graph.replay()
+        sync()
+        o_ref, l_ref, _ = decode(d, ns)
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), rep
+
+
+def test_decode_alternating_inputs_share_a_workspace():
+    # Two input sets through one workspace, alternately: every call gives the
+    # result of its own inputs (a stale partial from the other set would show).
+    B, H, ns = 4, 128, 32
+    lens = [3000, 700, 4100, 64]
+    dA = workloads.decode_inputs(B, H, lens, S_max=4100, seed=2810)
+    dB = workloads.decode_inputs(B, H, lens, S_max=4100, seed=2811)
+    ins = [tuple(d[k].to(DEV) for k in ("q_lat", "q_rope", "cache", "seqlens")) for d in (dA, dB)]
+    ws = binding.alloc_decode_workspace(B, H, ns, DEV)
+    first = []
+    for i in range(8):
+        o, l = binding.mla_decode_fwd(*ins[i % 2], SCALE, ns, workspace=ws)
+        sync()
+        if i < 2:
+            first.append((o.clone(), l.clone()))
+        else:
+            assert torch.equal(o, first[i % 2][0]) and torch.equal(l, first[i % 2][1]), i
+    plan = binding.read_plan(ws, B)
+    assert max(plan["nsplit"]) >= 2, plan["nsplit"]
+    Or, Lr = oracle_decode(dB)
+    check_bf16(first[1][0], Or, "O set B")
+    check_lse(first[1][1], Lr, "LSE set B")
