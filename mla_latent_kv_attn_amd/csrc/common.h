@@ -243,6 +243,29 @@ __device__ __forceinline__ float sum2_halves(float x) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Inclusive prefix sum and maximum over the 64 lanes of a wave with DPP row
+// shifts (within rows of 16 lanes) and row broadcasts (lane 15 into the next
+// row, lane 31 into rows 2 and 3); verified against a host reference on the
+// device.  dpp_wave_max returns the maximum in every lane.
+__device__ __forceinline__ int dpp_incl_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+__device__ __forceinline__ int dpp_wave_max(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x111, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x112, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x118, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Workgroup barrier for LDS hand-offs in the tile loops.  The wave's own
 // direct-to-LDS copies are waited for explicitly (wait_vmcnt) before it, and
 // its LDS reads are drained here (lgkmcnt 0), so no memory fence -- which

@@ -91,7 +91,7 @@ struct PlanArgs {
 //    num_splits == 1 each sequence gets its own part (t = max_n + c0).
 //    A block of 256 threads scans the lengths: each thread handles four
 //    consecutive sequences of a 1024-sequence chunk, so the offsets need one
-//    scan per chunk (within each wave by lane shuffles, then over the four
+//    scan per chunk (within each wave by DPP lane shifts, then over the four
 //    wave totals).  The first sequence of each part is found with LDS
 //    atomics.
 //    Where it runs: with num_splits >= 2 and B <= 1024 every split workgroup
@@ -104,25 +104,6 @@ constexpr int PLAN_THREADS = 256;
 constexpr int PLAN_PER = 4;
 constexpr int PLAN_CHUNK = PLAN_THREADS * PLAN_PER;
 static_assert(PLAN_THREADS == 256, "the split kernel's block runs the in-kernel plan");
-
-__device__ __forceinline__ int wave_incl_sum(int x, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d, 64));
-    return x;
-}
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
-}
 
 // One chunk of the cost-line scan: thread tid handles sequences
 // base + 4 tid + k (k < 4).  Returns their clamped lengths, tiles and
@@ -152,15 +133,15 @@ __device__ ChunkScan plan_scan_chunk(const int* __restrict__ seqlens, int base, 
         cost[k] = n[k] > 0 ? n[k] + c0 : 0;
         sum += cost[k];
     }
-    const int incl = wave_incl_sum(sum, lane);
-    mx = wave_max(mx);
-    ncl = wave_sum(ncl);
+    const int incl = dpp_incl_sum(sum);
+    mx = dpp_wave_max(mx);
+    ncl = __builtin_amdgcn_readlane(dpp_incl_sum(ncl), 63);
     if (lane == 63) s_red[wv] = incl;
     if (lane == 0) {
         s_red[NW + wv] = mx;
         s_red[2 * NW + wv] = ncl;
     }
-    __syncthreads();
+    lds_barrier();  // LDS only: no wait for this block's global stores
     int woff = 0;
     ChunkScan r{0, 0, 0};
 #pragma unroll
@@ -170,7 +151,7 @@ __device__ ChunkScan plan_scan_chunk(const int* __restrict__ seqlens, int base, 
         r.max_n = max(r.max_n, s_red[NW + i]);
         r.clamped += s_red[2 * NW + i];
     }
-    __syncthreads();  // s_red is rewritten by the next chunk
+    lds_barrier();  // s_red is rewritten by the next chunk
     int acc = carry + woff + incl - sum;  // cost of all sequences before this thread's first
 #pragma unroll
     for (int k = 0; k < PLAN_PER; ++k) {
@@ -876,7 +857,7 @@ __device__ void dec_plan_in_kernel(const DecodeCtx& x, char* smem, int p, int& t
     if (tid == 0) *s_b0 = B;
     if (writer)
         for (int q = tid; q < x.parts; q += PLAN_THREADS) s_pfs[q] = B;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < PLAN_PER; ++k) {
         const int b = PLAN_PER * tid + k;
@@ -897,7 +878,7 @@ __device__ void dec_plan_in_kernel(const DecodeCtx& x, char* smem, int p, int& t
             for (int q = first; q < first + ns; ++q) atomicMin(&s_pfs[q], b);
         }
     }
-    __syncthreads();
+    lds_barrier();
     b0 = *s_b0;
     if (writer) {
         for (int q = tid; q < x.parts; q += PLAN_THREADS) x.ws[x.a.part_first_seq + q] = s_pfs[q];
@@ -905,7 +886,7 @@ __device__ void dec_plan_in_kernel(const DecodeCtx& x, char* smem, int p, int& t
             plan_write_header(x.ws, parts_used, t, C, c0, false, x.parts, cs.clamped, cs.max_n, B, x.t_min,
                               x.num_splits);
     }
-    __syncthreads();  // the ring's scratch is free again
+    lds_barrier();  // the ring's scratch is free again (the plan record's stores need not have landed)
 }
 
 // Pieces of part p, found without a chain of dependent loads: lane i reads
