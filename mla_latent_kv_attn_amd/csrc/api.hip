@@ -56,10 +56,10 @@ inline bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 // (loading its query block, filling and draining the tile pipeline, writing
 // its output), in 32-token plan tiles.  Timestamps per workgroup on MI355X
 // (256 sequences of 256..8192 tokens) put that cost at about 15 us, against
-// about 1.9 us per 32-token step; c0 = 8 (256 tokens) measured fastest in a
-// sweep of 6..12 tokens-equivalent (308.6 us per call against 312.2 us for
-// 12).  t_min keeps parts from becoming so short that the fixed cost
-// dominates.
+// about 1.9 us per 32-token step; c0 = 8 (256 tokens) measured fastest
+// among 6, 8, 10 and 12 (321.9 us per call on one box, against 322.8, 323.9
+// and 325.9 us; the 16 x 4096 batch is within 0.3 us for all four).  t_min
+// keeps parts from becoming so short that the fixed cost dominates.
 struct DecodeConfig {
     int parts, slots, c0, t_min;
 };
