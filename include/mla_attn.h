@@ -38,7 +38,12 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes and data types are plain ints with named values, so that any
+ * int a caller passes (say 99 to mla_status_string, or 7 as a dtype) is a
+ * valid argument that the library can reject; an enum type would make such
+ * values undefined on the C++ side. */
+typedef int mla_status_t;
+enum {
     MLA_OK = 0,
     MLA_ERR_NULL = 1,        /* a required pointer is NULL                     */
     MLA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
@@ -49,9 +54,10 @@ typedef enum {
     MLA_ERR_HIP = 6,         /* the HIP runtime reported an error              */
     MLA_ERR_SCRATCH = 7      /* mla_decode_fwd_noalloc: the call needs more
                                 than the fixed scratch                         */
-} mla_status_t;
+};
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+typedef int mla_dtype_t;
+enum { MLA_F32 = 0, MLA_BF16 = 1 };
 
 /*
  * attn_fwd - fused attention forward (prefill), [FA2-v2 blog] sections 1.1-3.5.

@@ -12,7 +12,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_attn.so")
+# MLA_ATTN_LIB names another build of the same library (the host-only
+# sanitizer build); by default the in-tree libmla_attn.so is loaded.
+_LIB_PATH = os.environ.get("MLA_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libmla_attn.so")
 _lib = None
 
 (MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP,

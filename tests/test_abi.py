@@ -155,3 +155,50 @@ def test_decode_noalloc_validation_codes(lib):
     assert call(scale=-1.0) == binding.MLA_ERR_SHAPE
     assert call(c=BAD) == binding.MLA_ERR_ALIGN
     assert call(lse=BAD) == binding.MLA_ERR_ALIGN
+
+
+INT_MIN, INT_MAX = -(1 << 31), (1 << 31) - 1
+EXTREMES = (INT_MIN, -1, 0, 1, 15, 16, 17, 1 << 16, (1 << 20) + 1, INT_MAX)
+
+
+def _sweep(fn, base, positions, allowed):
+    """Each listed int argument takes every extreme value in turn; a misaligned
+    pointer in `base` keeps every call from reaching a launch, so the status
+    is a validation code and never MLA_OK or MLA_ERR_HIP."""
+    for pos in positions:
+        for val in EXTREMES:
+            args = list(base)
+            args[pos] = val
+            st = fn(*args)
+            assert st in allowed, (fn.__name__, pos, val, st)
+
+
+def test_extreme_integer_arguments_are_rejected_before_any_launch(lib):
+    # Under the host sanitizer build these also check that no validation
+    # expression overflows or reads an out-of-range value.
+    shape = {binding.MLA_ERR_SHAPE, binding.MLA_ERR_UNSUPPORTED, binding.MLA_ERR_ALIGN}
+    _sweep(lib.attn_fwd, [P, P, P, BAD, P, 1, 2, 256, 64, 0.125, 0, 0, None], (5, 6, 7, 8, 10, 11), shape)
+    _sweep(lib.attn_fwd_chunk, [P, P, P, BAD, P, 1, 2, 128, 256, 128, 0.125, 1, 1, None], (5, 6, 7, 8, 9, 11, 12),
+           shape)
+    _sweep(lib.mla_decode_fwd, [BAD, P, P, P, P, P, 2, 128, 64, 0.04, 4, P, 1 << 30, None], (6, 7, 8, 10), shape)
+    _sweep(lib.mla_decode_fwd_v, [BAD, P, P, P, P, P, P, 2, 128, 64, 512, 0.04, 4, P, 1 << 30, None],
+           (7, 8, 9, 10, 12), shape)
+    _sweep(lib.mla_decode_fwd_noalloc, [BAD, P, P, P, P, P, 2, 128, 64, 0.04, 4, None], (6, 7, 8, 10), shape)
+    _sweep(lib.mla_combine, [BAD, P, P, P, 2, 128, 4, None], (4, 5, 6), shape)
+    _sweep(lib.mla_absorb_q, [BAD, P, P, 4, 8, 128, 512, None], (3, 4, 5, 6), shape)
+    _sweep(lib.mla_up_proj_v, [BAD, P, P, 4, 8, 512, 128, None], (3, 4, 5, 6), shape)
+
+
+def test_extreme_workspace_queries_and_status_codes(lib):
+    for fn in (lib.mla_decode_workspace_size, lib.mla_decode_v_workspace_size):
+        for pos in range(3):
+            for val in EXTREMES:
+                args = [4, 128, 4]
+                args[pos] = val
+                n = fn(*args)
+                valid = 1 <= args[0] <= 1 << 16 and args[1] >= 16 and args[1] % 16 == 0 and args[1] <= 1024 \
+                    and 1 <= args[2] <= 32
+                if not valid:
+                    assert n == 0, (fn.__name__, args, n)
+    for s in (INT_MIN, -1, 8, INT_MAX):
+        assert lib.mla_status_string(s).decode() == "unknown mla_status_t"
