@@ -289,7 +289,8 @@ def bench_decode_fixed(log, copies=8, reps=200):
     return {"workload": "mla_fixed: B=16, H=128, 4096 tokens each, num_splits<=32, "
                         f"{copies} rotating input copies (no Infinity Cache reuse)",
             "us": round(avg * 1e3, 2), "kv_bytes": kv_bytes, "GB_s": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "traffic": measured_traffic(log, PMC_SUMMARY_FIXED)}
 
 
 def chunk_pairs(Nq, Nk, causal):
@@ -329,8 +330,10 @@ def bench_prefill_chunk(log, B=4, H=16, Nq=1024, Nk=4096, D=128, seed=1007, cpu=
 # The decode kernels, their plan layout, and the host code that sets the plan
 # constants (the split count, and with it the partial traffic, depends on them).
 DECODE_SOURCES = ("mla_latent_kv_attn_amd/csrc/mla_decode.hip", "mla_latent_kv_attn_amd/csrc/mla_plan.h",
-                  "mla_latent_kv_attn_amd/csrc/common.h", "mla_latent_kv_attn_amd/csrc/api.hip")
+                  "mla_latent_kv_attn_amd/csrc/mla_merge.h", "mla_latent_kv_attn_amd/csrc/common.h",
+                  "mla_latent_kv_attn_amd/csrc/api.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_varlen_pmc.json")
+PMC_SUMMARY_FIXED = os.path.join(ROOT, "profiles", "mla_decode_fixed_pmc.json")
 
 
 def sources_sha():
@@ -357,11 +360,11 @@ def decode_sources_sha():
     return h.hexdigest()
 
 
-def measured_traffic(log):
-    """HBM bytes per decode call from the committed counter summary, or None
+def measured_traffic(log, path=PMC_SUMMARY):
+    """HBM bytes per decode call from a committed counter summary, or None
     when it was taken on different kernel sources than the ones built here."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
