@@ -74,3 +74,38 @@ def test_one_step_of_each_kind(asm):
     # (136) and one last step (64): nothing is duplicated by the compiler
     body = kernel_body(asm)
     assert sum(1 for l in body if l.startswith("v_mfma")) == 72 + 136 + 64
+
+
+def _vregs(operand):
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"v(\d+)", operand)
+    return {int(m.group(1))} if m else set()
+
+
+def test_valu_writes_reach_mfma_sources_two_wait_states_early(asm):
+    # The MFMAs are inline asm, so the compiler inserts no wait states for
+    # them.  A VGPR that a VALU instruction writes (for instance a move that
+    # joins the two halves of a value fragment) may be read as an MFMA
+    # source only two wait states later (s_nop N counts N + 1, any other
+    # instruction 1): the rule the compiler itself applies on gfx950.
+    body = [l for l in kernel_body(asm) if l and not l.startswith(".") and not l.endswith(":")]
+    bad = []
+    for i, line in enumerate(body):
+        if not line.startswith("v_mfma"):
+            continue
+        args = [a.strip() for a in line.partition(" ")[2].split(",")]
+        src = set().union(*(_vregs(a) for a in args[1:4]))
+        ws = 0
+        for j in range(i - 1, max(-1, i - 16), -1):
+            op, _, rest = body[j].partition(" ")
+            dst = rest.split(",")[0].strip() if rest else ""
+            if op.startswith("v_") and not op.startswith("v_mfma") and _vregs(dst) & src:
+                if ws < 2:
+                    bad.append((body[j], line))
+                break
+            ws += int(rest) + 1 if op == "s_nop" else 1
+            if ws >= 2:
+                break
+    assert not bad, bad[:4]
