@@ -220,3 +220,25 @@ def test_bf16_chunk_at_benchmark_shape():
     check_bf16(torch.stack([o[b, h] for b, h in sl]), Or, "O(whole slices)")
     check_lse(torch.stack([l[b, h] for b, h in sl]), Lr, "LSE(whole slices)")
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_rising_scores_rescale_every_tile(causal):
+    # Scores rise by about 12 (log2 units) per 64-key tile for every query:
+    # all queries share a direction u and key j carries u times a ramp in j,
+    # so the exponent base moves on every tile and the accumulators are
+    # rescaled.  Values stay N(0,1).
+    B, H, N, D = 1, 2, 512, 128
+    q, k, v = workloads.attn_inputs(B, H, N, D, torch.float32, seed=2201)
+    g = torch.Generator().manual_seed(2202)
+    u = torch.randn(D, generator=g) / math.sqrt(D)
+    scale = 1 / math.sqrt(D)
+    kappa = 12.0 / (scale * 3.0 * float(u @ u) * 1.4426950408889634)
+    q = 3.0 * u + 0.3 * q
+    k = k + (torch.arange(N, dtype=torch.float32)[:, None] / 64.0) * kappa * u
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    say(f"bf16 rising scores causal={causal}")
+    o, l = run(q, k, v, scale, causal)
+    Or, Lr = OA.attn_ref(np64(q), np64(k), np64(v), scale, causal)
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")

@@ -505,3 +505,38 @@ def test_decode_alternating_inputs_share_a_workspace():
     Or, Lr = oracle_decode(dB)
     check_bf16(first[1][0], Or, "O set B")
     check_lse(first[1][1], Lr, "LSE set B")
+
+
+def _ramped_decode_inputs(B, H, lens, S_max, seed, per_tile_log2=12.0):
+    """Decode inputs whose scores rise by about per_tile_log2 (log2 units)
+    every 32 tokens, for every head, so that the exponent base moves on every
+    tile and the accumulators are rescaled: the rope parts of all heads'
+    queries share a direction u, and each cached row's rope part is u times
+    a ramp in the token index.  The latent part (the values) stays N(0,1)."""
+    d = workloads.decode_inputs(B, H, lens, S_max=S_max, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    u = torch.randn(64, generator=g) / 8.0                      # |u| about 1
+    qr = 3.0 * u + 0.3 * torch.randn((B, H, 64), generator=g)
+    d["q_rope"] = qr.to(torch.bfloat16)
+    # score from the ramp: SCALE * 3 |u|^2 * kappa per tile, times log2(e)
+    kappa = per_tile_log2 / (SCALE * 3.0 * float(u @ u) * 1.4426950408889634)
+    for b, L in enumerate(lens):
+        t = torch.arange(L, dtype=torch.float32)[:, None]
+        d["cache"][b, :L, 512:] = (d["cache"][b, :L, 512:].float() + (t / 32.0) * kappa * u).to(torch.bfloat16)
+    return d
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 32])
+def test_decode_rising_scores_rescale_every_tile(num_splits):
+    # Every tile's max exceeds the exponent base by more than the lazy-rescale
+    # slack, so each step runs the accumulator rescale (alpha < 1), in every
+    # piece of a split sequence too.
+    lens = [300, 1000, 33]
+    say(f"decode rising scores lens={lens} num_splits={num_splits}")
+    d = _ramped_decode_inputs(3, 128, lens, 1024, seed=2101)
+    o, l, ws = decode(d, num_splits)
+    check_plan(ws, d, num_splits)
+    Or, Lr = oracle_decode(d)
+    assert float(np.abs(Lr - Lr.mean()).max()) > 50, "the ramp reaches far above the first tile"
+    check_bf16(o, Or, "O")
+    check_lse(l, Lr, "LSE")
