@@ -16,6 +16,11 @@ prefill = bf16 causal prefill (B=4 H=16 N=4096 D=128) and the fp32
         vector-ALU prefill (B=4 H=8 N=8192 D=64), TFLOP/s vs their peaks.
 cpu_baseline = the fp64 oracle on a bounded sample of the same decode
         workload, timed on this host's cores.
+power = socket power, shader clock and energy per call of each GPU leg,
+        sampled (read-only amdsmi queries) over a separate ~1 s loop of the
+        leg after its timed region, and the bf16 MFMA rate this board
+        sustains under its power limit (a calibration kernel of back-to-back
+        MFMAs on register data, libmla_calib.so); null without amdsmi.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--no-cpu] [--no-prefill]
 
@@ -91,7 +96,127 @@ def time_events(fn, reps):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def bench_decode(args, log):
+class PowerSampler:
+    """Socket power, shader clock and power-limit residency of a loop of GPU
+    calls, from read-only amdsmi queries on the device that cuda:0 is
+    (matched by PCI bus).  Unavailable (every result None) when amdsmi cannot
+    be used.  The firmware's accumulation counter ticks once per millisecond;
+    its PPT residency counter ticks in the milliseconds during which the
+    package-power limiter held the clock down."""
+
+    THERMAL = ("socket_thm_residency_acc", "vr_thm_residency_acc", "hbm_thm_residency_acc", "prochot_residency_acc")
+
+    def __init__(self):
+        self.smi = self.h = None
+        self.cap_w = None
+        try:
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init()
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if bus is None or int(bdf.split(":")[1], 16) == bus:
+                    self.smi, self.h = amdsmi, h
+                    break
+            if self.smi is not None:
+                self.cap_w = self.smi.amdsmi_get_power_cap_info(self.h)["power_cap"] / 1e6
+        except Exception:
+            self.smi = self.h = None
+
+    def _counters(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        return (m["accumulation_counter"], m["ppt_residency_acc"], sum(m[k] for k in self.THERMAL))
+
+    def run(self, fn, seconds=1.0, per_sync=10, settle=0.3):
+        """Run fn back to back for `seconds` (after `settle` seconds) while a
+        thread samples the socket power and the shader clock every 20 ms."""
+        if self.smi is None:
+            return None
+        import threading
+        import torch
+        warm(fn, settle)
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                try:
+                    m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+                    samples.append((m["current_socket_power"], m["current_gfxclk"]))
+                except Exception:
+                    pass
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        try:
+            c0 = self._counters()
+            th.start()
+            t0, calls = time.perf_counter(), 0
+            while time.perf_counter() - t0 < seconds:
+                for _ in range(per_sync):
+                    fn()
+                torch.cuda.synchronize()
+                calls += per_sync
+            t1 = time.perf_counter()
+            stop.set()
+            th.join()
+            c1 = self._counters()
+        except Exception:
+            stop.set()
+            return None
+        if not samples:
+            return None
+        n = len(samples)
+        watts = sum(p for p, _ in samples) / n
+        us = (t1 - t0) / calls * 1e6
+        ticks = max(c1[0] - c0[0], 1)
+        return {"socket_W": round(watts, 1), "gfxclk_MHz": round(sum(c for _, c in samples) / n),
+                "ppt_limited": round((c1[1] - c0[1]) / ticks, 3), "thermal_limited": round((c1[2] - c0[2]) / ticks, 3),
+                "mJ_per_call": round(watts * us * 1e-3, 3), "us_per_call": round(us, 2), "calls": calls,
+                "samples": n}
+
+
+def mfma_ceiling(log, ps, seconds=1.5):
+    """The bf16 MFMA rate this board sustains: the calibration kernel
+    (back-to-back MFMAs on register data, 8 waves per CU) run for `seconds`
+    per shape, with power and clock sampled meanwhile."""
+    import ctypes
+    import torch
+    from mla_latent_kv_attn_amd import build as _b
+    if ps.smi is None or not os.path.exists(_b.CALIB_LIB):
+        return None
+    lib = ctypes.CDLL(_b.CALIB_LIB)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.mla_calib_mfma_rate.argtypes = [vp, vp, i, i, i, vp]
+    lib.mla_calib_mfma_rate.restype = i
+    g = torch.Generator().manual_seed(11)
+    tables = {"N(0,1)": torch.randn(65536 * 8, generator=g).to(torch.bfloat16).to("cuda:0"),
+              "zero": torch.zeros(65536 * 8, dtype=torch.bfloat16, device="cuda:0")}
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for shape, flop, iters, operands in ((16, 16384, 6000, "N(0,1)"), (32, 32768, 3000, "N(0,1)"),
+                                         (16, 16384, 6000, "zero")):
+        table = tables[operands]
+
+        def fn():
+            r = lib.mla_calib_mfma_rate(table.data_ptr(), out.data_ptr(), blocks, iters, shape, st)
+            if r != 0:
+                raise RuntimeError(f"calibration launch failed: hipError {r}")
+        p = ps.run(fn, seconds=seconds, per_sync=2)
+        if p is None:
+            return None
+        tf = blocks * 4 * iters * 64 * flop / (p["us_per_call"] * 1e-6) / 1e12
+        name = f"{shape}x{shape}x{512 // shape}" + ("" if operands == "N(0,1)" else " zero operands")
+        res[name] = dict(TFLOP_s=round(tf, 1), frac_of_peak=round(tf / BF16_PEAK_TFLOPS, 4), operands=operands, **p)
+        log(f"bf16 MFMA ceiling ({shape}x{shape}x{512 // shape}, {operands} operands, 8 waves/CU): {tf:.0f} TFLOP/s at "
+            f"{p['gfxclk_MHz']} MHz, {p['socket_W']} W, power-limited {p['ppt_limited']:.0%}")
+    del tables, out
+    return res
+
+
+def bench_decode(args, log, ps=None):
     import torch
     from mla_latent_kv_attn_amd import binding, workloads
     dev = "cuda:0"
@@ -176,7 +301,8 @@ def bench_decode(args, log):
     log(f"value up-projection: {up_ms*1e3:.1f} us ({up_bytes/(up_ms*1e-3)/1e9:.0f} GB/s); decode + W_UV fused "
         f"{dv_ms*1e3:.1f} us, unfused {uf_ms*1e3:.1f} us (medians)")
     dec_sorted = sorted(dec_ms)
-    return dict(workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
+    power = ps.run(decode) if ps else None
+    return dict(power=power, workload=w, lens=lens, kv_bytes=kv_bytes, ms_step=ms_step, dec_ms=dec_avg, abs_ms=abs_avg,
                 dec_median=dec_sorted[len(dec_sorted) // 2], dec_min=dec_sorted[0],
                 absorb_bytes=absorb_bytes, plan=plan, up_ms=up_ms, up_bytes=up_bytes, dv_ms=dv_ms, uf_ms=uf_ms,
                 warm_s=warm_s, warm_calls=warm_calls)
@@ -216,7 +342,7 @@ def cpu_prefill_oracle(log, q, k, v, scale, causal, what, budget_s=3.0):
                       f"{elapsed:.1f} s"}
 
 
-def bench_prefill(log, name, causal, reps=None, cpu=False):
+def bench_prefill(log, name, causal, reps=None, cpu=False, ps=None):
     import torch
     from mla_latent_kv_attn_amd import binding, workloads
     dev = "cuda:0"
@@ -238,6 +364,8 @@ def bench_prefill(log, name, causal, reps=None, cpu=False):
             "ms": round(avg, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4), "tflops": round(tf, 2),
             "peak_tflops": peak, "frac": round(tf / peak, 4),
             "bound": "mfma" if w["dtype"] == torch.bfloat16 else "alu"}
+    if ps:
+        line["power"] = ps.run(fn)
     if cpu:
         del q, k, v, o, lse
         line["cpu_oracle"] = cpu_prefill_oracle(log, w["q"], w["k"], w["v"], w["scale"], causal,
@@ -245,7 +373,7 @@ def bench_prefill(log, name, causal, reps=None, cpu=False):
     return line
 
 
-def bench_decode_fixed(log, copies=8, reps=200):
+def bench_decode_fixed(log, copies=8, reps=200, ps=None):
     """MLA decode on the fixed-length batch (16 sequences x 4096 tokens, 128
     heads, num_splits 32).  Its 75.5 MB cache fits in the 256 MB Infinity
     Cache, so successive calls rotate over `copies` separate copies of the
@@ -286,7 +414,8 @@ def bench_decode_fixed(log, copies=8, reps=200):
     avg = sum(ms) / len(ms)
     gbs = kv_bytes / (avg * 1e-3) / 1e9
     log(f"decode mla_fixed (16 x 4096, rotating {copies} input copies): {avg*1e3:.1f} us, {gbs:.0f} GB/s")
-    return {"workload": "mla_fixed: B=16, H=128, 4096 tokens each, num_splits<=32, "
+    power = ps.run(rot, per_sync=50) if ps else None
+    return {"power": power, "workload": "mla_fixed: B=16, H=128, 4096 tokens each, num_splits<=32, "
                         f"{copies} rotating input copies (no Infinity Cache reuse)",
             "us": round(avg * 1e3, 2), "kv_bytes": kv_bytes, "GB_s": round(gbs, 1),
             "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
@@ -385,7 +514,7 @@ def plain_copy():
     print(f"copied {n} bytes 3 times", file=sys.stderr, flush=True)
 
 
-def copy_bandwidth(log, nbytes=1 << 30, reps=20):
+def copy_bandwidth(log, nbytes=1 << 30, reps=20, ps=None):
     """Attainable HBM rate of a plain device copy (context for the roofline):
     bytes read + bytes written per copy / time."""
     import torch
@@ -398,8 +527,9 @@ def copy_bandwidth(log, nbytes=1 << 30, reps=20):
     avg = sum(ms) / len(ms)
     gbs = 2 * nbytes / (avg * 1e-3) / 1e9
     log(f"device copy of {nbytes >> 20} MiB: {avg*1e3:.1f} us, {gbs:.0f} GB/s (read + write)")
+    power = ps.run(lambda: b.copy_(a), per_sync=4) if ps else None
     del a, b
-    return round(gbs, 1)
+    return round(gbs, 1), power
 
 
 def cpu_baseline(d, log, budget_s=12.0):
@@ -483,18 +613,32 @@ def main():
     if args.only == "prefill_fp32":
         bench_prefill(log, "attn_fp32", False, reps=args.steps)
         return
-    d = bench_decode(args, log)
+    ps = None if args.only == "decode" else PowerSampler()
+    d = bench_decode(args, log, ps)
     if args.only == "decode":
         return
-    decode_fixed = bench_decode_fixed(log)
-    copy_gbs = copy_bandwidth(log)
+    decode_fixed = bench_decode_fixed(log, ps=ps)
+    copy_gbs, copy_power = copy_bandwidth(log, ps=ps)
     prefill = {}
     if not args.no_prefill:
         cpu = not args.no_cpu
-        prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True, cpu=cpu)
+        prefill["bf16_causal"] = bench_prefill(log, "attn_bf16", True, cpu=cpu, ps=ps)
         prefill["fp32_noncausal"] = bench_prefill(log, "attn_fp32", False, reps=5, cpu=cpu)
         prefill["fp32_causal"] = bench_prefill(log, "attn_fp32", True, reps=5, cpu=cpu)
         prefill["bf16_chunk"] = bench_prefill_chunk(log, cpu=cpu)
+    ceiling = mfma_ceiling(log, ps)
+    power = None
+    if ps.smi is not None:
+        power = {"cap_W": ps.cap_w, "decode": d["power"], "decode_fixed": decode_fixed.pop("power"),
+                 "bf16_causal": prefill.get("bf16_causal", {}).pop("power", None), "copy": copy_power,
+                 "mfma_bf16_ceiling": ceiling,
+                 "note": "each leg re-run for ~1 s after its timed region; socket power and shader clock "
+                         "sampled every 20 ms (amdsmi, read-only); ppt_limited = share of the firmware's 1 ms "
+                         "ticks in which the package-power limiter was active; mJ_per_call = socket_W x "
+                         "us_per_call"}
+    else:
+        decode_fixed.pop("power", None)
+        prefill.get("bf16_causal", {}).pop("power", None)
     cpu = None if args.no_cpu else cpu_baseline(d, log)
     value = d["kv_bytes"] / (d["ms_step"] * 1e-3) / 1e9
     achieved = d["kv_bytes"] / (d["dec_ms"] * 1e-3) / 1e9
@@ -535,6 +679,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_fixed": decode_fixed,
         "prefill": prefill,
+        "power": power,
     }
     print(json.dumps(line), flush=True)
 

@@ -202,3 +202,24 @@ def test_extreme_workspace_queries_and_status_codes(lib):
                     assert n == 0, (fn.__name__, args, n)
     for s in (INT_MIN, -1, 8, INT_MAX):
         assert lib.mla_status_string(s).decode() == "unknown mla_status_t"
+
+
+def test_calibration_library_exports_its_kernel_and_checks_arguments():
+    # The benchmark's MFMA-rate calibration kernel lives in its own library,
+    # next to (not inside) the attention library.
+    from mla_latent_kv_attn_amd import build as _b
+    if not os.path.exists(_b.CALIB_LIB):
+        pytest.skip("libmla_calib.so not built")
+    cal = ctypes.CDLL(_b.CALIB_LIB)
+    f = cal.mla_calib_mfma_rate
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, vp, i, i, i, vp]
+    f.restype = i
+    bad = 1  # hipErrorInvalidValue
+    p = ctypes.c_void_p(16)
+    assert f(None, p, 1, 1, 16, None) == bad
+    assert f(p, None, 1, 1, 16, None) == bad
+    assert f(p, p, 0, 1, 16, None) == bad
+    assert f(p, p, 1, 0, 32, None) == bad
+    assert f(p, p, 1, 1, 8, None) == bad
+    assert not hasattr(binding.load(), "mla_calib_mfma_rate")
