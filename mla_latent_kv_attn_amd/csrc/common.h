@@ -99,6 +99,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)lds_wave_base, 16, (int)voff, 0, 0, 0);
 }
+// The same copy with the non-temporal cache policy bit (nt): for data read
+// exactly once, such as the decode's cache rows, so that the caches keep the
+// lines that are read again (queries, split partials) instead.
+__device__ __forceinline__ void bload_lds16_stream(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voff) {
+    constexpr int kNonTemporal = 2;  // cache policy operand: nt
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)lds_wave_base, 16, (int)voff, 0, 0, kNonTemporal);
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).

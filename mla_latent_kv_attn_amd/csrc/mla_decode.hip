@@ -21,7 +21,8 @@
 // Split-kernel design.  A workgroup is 4 waves, one per SIMD, and serves 128
 // heads, so every cache byte crosses HBM -> LDS once for all of them.  The
 // cache streams through a ring of four 32-token LDS tiles (37,888 B each)
-// filled by buffer_load ... lds.  Wave w owns heads 32w..32w+31 for the whole
+// filled by buffer_load ... lds (non-temporal: every cache row is read once).
+// Wave w owns heads 32w..32w+31 for the whole
 // computation:
 //   * their q fragments stay in VGPRs (32 heads x 576 bf16 = 144 VGPRs);
 //   * S^T = C q^T on v_mfma_f32_16x16x32_bf16, every cache fragment read from
@@ -683,9 +684,9 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
                     constexpr int c = 2 * Sch::kpos(t) + (m - 2);  // copy number of this slot
                     static_assert(kind == 0 && m >= 2 && c >= 0, "copies sit in the last two slots of K groups");
                     if constexpr (c < DEC_LOADS_LO) {
-                        bload_lds16(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
+                        bload_lds16_stream(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
                     } else if constexpr (c < DEC_LOADS_HI) {
-                        if (w < DEC_LOADS_EXTRA) bload_lds16(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
+                        if (w < DEC_LOADS_EXTRA) bload_lds16_stream(rsrc, dst + (w + DEC_WAVES * c) * 1024, voff[c]);
                     }
                 }
                 constexpr int d = Sch::slot0(t) + m - smx0;
@@ -724,7 +725,7 @@ __device__ void dec_piece(const DecodeCtx& x, char* smem, int p, int b, int tile
         const auto r = tile_rsrc(i);
         static_for<DEC_LOADS_HI>([&](auto k_c) {
             constexpr int k = decltype(k_c)::value;
-            if (k < DEC_LOADS_LO || w < DEC_LOADS_EXTRA) bload_lds16(r, smem + i * DEC_TILE_BYTES + (w + DEC_WAVES * k) * 1024, voff[k]);
+            if (k < DEC_LOADS_LO || w < DEC_LOADS_EXTRA) bload_lds16_stream(r, smem + i * DEC_TILE_BYTES + (w + DEC_WAVES * k) * 1024, voff[k]);
         });
     }
     top(0);
