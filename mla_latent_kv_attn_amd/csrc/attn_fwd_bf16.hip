@@ -326,23 +326,32 @@ __global__ __launch_bounds__(B16_THREADS, 2) void attn_fwd_bf16_kernel(
     wait_vmcnt<0>();
 
     // Epilogue: O = Oacc / l; O^T register e of block db: dim 32db + 8(e/4) + 4g + e%4.
+    // The rows go through LDS (the K/V buffers, free once every wave's last
+    // copies have landed) so that each store writes four whole 256-byte rows.
+    lds_barrier();
     l = sum2_halves(l);
     const int row = wrow0 + n;
-    if (row < Nq) {
-        // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
-        const float inv_l = l > 0.f ? 1.f / l : 0.f;
-        __bf16* op = o + base + (size_t)row * B16_D;
+    // A row that saw no key (l = 0, only with Nq > Nk) gets O = 0, LSE = -inf.
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+    constexpr int STG = 272;  // staging row stride (bytes): 256 + 16 against bank conflicts
+    char* stg = &smem[0][0][0] + w * 32 * STG;
 #pragma unroll
-        for (int db = 0; db < B16_D / 32; ++db)
+    for (int db = 0; db < B16_D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bf16x4 t;
+        for (int i = 0; i < 4; ++i) {
+            bf16x4 t;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][4 * i + r] * inv_l);
-                *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i + 4 * g) = t;
-            }
-        if (lse && g == 0) lse[(size_t)bh * Nq + row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
+            for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[db][4 * i + r] * inv_l);
+            *reinterpret_cast<bf16x4*>(stg + n * STG + 2 * (32 * db + 8 * i + 4 * g)) = t;
+        }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): the wave's rows are in LDS
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8) {
+        const int r = 4 * k8 + (lane >> 4), c = lane & 15;
+        const bf16x8 vrow = *reinterpret_cast<const bf16x8*>(stg + r * STG + 16 * c);
+        if (wrow0 + r < Nq) *reinterpret_cast<bf16x8*>(o + base + (size_t)(wrow0 + r) * B16_D + 8 * c) = vrow;
     }
+    if (lse && g == 0 && row < Nq) lse[(size_t)bh * Nq + row] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_attn_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o, float* lse,

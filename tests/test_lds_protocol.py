@@ -195,13 +195,15 @@ def decode_split_kernel(pieces, nbuf=4, ahead=2, epilogue_vm_wait=True, trailing
     return w
 
 
-def prefill_bf16_kernel(T):
+def prefill_bf16_kernel(T, epilogue_barrier=True):
     """attn_fwd_bf16_kernel: K and V of tile j in buffer j % 2.  Tile 0 is
     copied before the loop; step j waits for every copy of this wave and
     passes a draining barrier, reads K of tile j while it copies tile j+1
     into the other buffer (one K or V copy per score k-step; a tile past
     the end copies zeros), reads V of tile j, and ends with a draining
-    barrier.  The last step's copies land before the kernel ends."""
+    barrier.  The epilogue waits for the last step's copies, passes a
+    draining barrier, writes the wave's output rows into its own staging
+    rows over both buffers and reads them back for whole-row stores."""
     w = Wave()
     for kv in ("K", "V"):
         w.copy((kv, 0), 0)
@@ -216,6 +218,17 @@ def prefill_bf16_kernel(T):
         w.wait_lgkm()
         w.barrier(drain_lds=True)
     w.wait_vm()
+    if epilogue_barrier:
+        w.barrier(drain_lds=True)
+    out = T + 1  # a version after every tile copy, including the empty tile T
+    for b in range(2):
+        for kv in ("K", "V"):
+            w.write((kv, b), out, private=True)
+    w.wait_lgkm()
+    for b in range(2):
+        for kv in ("K", "V"):
+            w.read((kv, b), out, "staging", private=True)
+    w.wait_lgkm()
     w.end()
     return w
 
@@ -262,6 +275,13 @@ def test_decode_split_kernel_protocol_is_race_free(pieces):
 @pytest.mark.parametrize("T", [1, 2, 3, 8])
 def test_prefill_bf16_protocol_is_race_free(T):
     assert check(prefill_bf16_kernel(T)) == []
+
+
+def test_prefill_epilogue_without_its_barrier_races_other_waves_copies():
+    # A wave that has waited only for its own copies may stage its rows over
+    # a buffer into which another wave's last (empty-tile) copies still land.
+    issues = check(prefill_bf16_kernel(3, epilogue_barrier=False))
+    assert any(i[0] == "order" and i[3] == 4 for i in issues), issues
 
 
 def test_decode_three_slot_ring_with_two_tiles_in_flight_overwrites_the_values_tile():
