@@ -636,6 +636,13 @@ def main():
         prefill["fp32_causal"] = bench_prefill(log, "attn_fp32", True, reps=5, cpu=cpu)
         prefill["bf16_chunk"] = bench_prefill_chunk(log, cpu=cpu)
     ceiling = mfma_ceiling(log, ps)
+    if ceiling and "32x32x16" in ceiling:
+        # The bf16 prefill kernels issue 32x32x16 MFMAs: their rate against what
+        # the calibration loop of that shape sustains on this board.
+        top = ceiling["32x32x16"]["TFLOP_s"]
+        for key in ("bf16_causal", "bf16_chunk"):
+            if key in prefill:
+                prefill[key]["frac_of_mfma_loop"] = round(prefill[key]["tflops"] / top, 4)
     power = None
     if ps.smi is not None:
         power = {"cap_W": ps.cap_w, "decode": d["power"], "decode_fixed": decode_fixed.pop("power"),
