@@ -121,8 +121,10 @@ size_t mla_decode_workspace_size(int B, int H, int num_splits);
  * sequence is split across compute units (at most num_splits pieces per
  * sequence) by an on-device planner; pieces write partials (bf16 outputs
  * normalised by their own weight sum, fp32 LSE) to the workspace and a
- * log-sum-exp combine merges them.  Three kernels are
- * enqueued (plan, split, combine); none waits on the host.
+ * log-sum-exp combine merges them.  Two or three kernels are enqueued: the
+ * split kernel (which computes the plan itself when num_splits >= 2 and
+ * B <= 1024; otherwise a one-workgroup plan kernel runs first) and the
+ * combine.  None waits on the host.
  *
  * q_lat    : [B, H, 512] bf16      q_rope : [B, H, 64] bf16
  * kv_cache : [B, S_max, 576] bf16; token t of sequence b is row b*S_max + t.
